@@ -1,0 +1,166 @@
+"""Python binding of the NVFP4 W4A4 linear-layer library (libnvfp4.so).
+
+Argument marshalling only: every operation runs in the HIP kernels behind the
+C ABI declared in include/nvfp4.h.  torch provides device memory and the
+current stream; there is no fallback path: if the library is missing or no
+GPU is visible, the calls raise.
+
+Functions carry the C names:
+  nvfp4_quantize(x, gscale, mode)            -> (codes, scales)
+  nvfp4_fuse_rescale(scales, k, rows, gs)    -> (g_star, lossy_blocks)
+  nvfp4_gemm(a_codes, a_scales, a_gscale,
+             w_codes, w_scales, w_gscale,
+             out_dtype)                      -> c
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnvfp4.so")
+
+NVFP4_OK = 0
+STATUS_NAMES = {0: "NVFP4_OK", 1: "NVFP4_ERR_NULL", 2: "NVFP4_ERR_SHAPE", 3: "NVFP4_ERR_ALIGN",
+                4: "NVFP4_ERR_DTYPE", 5: "NVFP4_ERR_RANGE", 6: "NVFP4_ERR_DEVICE"}
+F32, BF16, F16 = 0, 1, 2
+GSCALE_STATIC, GSCALE_DYNAMIC = 0, 1
+MAX_FUSED_MODULES = 64
+
+# every symbol include/nvfp4.h declares, with (restype, argtypes)
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+SIGNATURES = {
+    "nvfp4_quantize": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _I32, _P, _P, _P]),
+    "nvfp4_fuse_rescale": (_I32, [_P, _I64, _I32, _P, _P, _P, _P, _P]),
+    "nvfp4_gemm": (_I32, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _P]),
+    "nvfp4_status_str": (ctypes.c_char_p, [_I32]),
+    "nvfp4_abi_version": (_I32, []),
+}
+
+_lib = None
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)} ({msg})")
+        self.status = status
+
+
+def load_library(path: str | None = None):
+    """Load libnvfp4.so (built in-tree by build.build()); raises if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().nvfp4_status_str(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != NVFP4_OK:
+        raise Nvfp4Error(fn, status, status_str(status))
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(dtype) -> int:
+    torch = _torch()
+    table = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+    if dtype not in table:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return table[dtype]
+
+
+def _stream_ptr(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t.data_ptr()
+
+
+def nvfp4_quantize(x, gscale, mode: str = "static", codes=None, scales=None, stream=None):
+    """Quantise a 2-D GPU tensor x (f32 / bf16 / f16, unit stride along columns).
+
+    gscale: GPU float32 tensor with one element; read (mode='static') or
+    written (mode='dynamic').  Returns (codes uint8 [rows, cols/2],
+    scales uint8 [rows, cols/16]).
+    """
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=x.device)
+    m = {"static": GSCALE_STATIC, "dynamic": GSCALE_DYNAMIC}[mode]
+    st = load_library().nvfp4_quantize(_dev(x, "x"), _dtype_code(x.dtype), rows, cols, x.stride(0),
+                                       _dev(gscale, "gscale"), m, _dev(codes, "codes"), _dev(scales, "scales"),
+                                       _stream_ptr(stream))
+    _check("nvfp4_quantize", st)
+    return codes, scales
+
+
+def nvfp4_fuse_rescale(scales, k: int, module_rows, module_gscales, want_lossy: bool = True, stream=None):
+    """Rewrite the stacked block scales of a fused group in place.
+
+    Returns (g_star, lossy) where g_star is the shared encode scale (float)
+    and lossy a GPU int64 tensor [1] (or None) counting changed blocks.
+    """
+    torch = _torch()
+    n = len(module_rows)
+    rows_arr = (ctypes.c_int64 * n)(*[int(r) for r in module_rows])
+    gs_arr = (ctypes.c_float * n)(*[float(g) for g in module_gscales])
+    g_star = ctypes.c_float(0.0)
+    lossy = torch.empty(1, dtype=torch.int64, device=scales.device) if want_lossy else None
+    st = load_library().nvfp4_fuse_rescale(_dev(scales, "scales"), int(k), n, ctypes.cast(rows_arr, _P),
+                                           ctypes.cast(gs_arr, _P), ctypes.addressof(g_star),
+                                           None if lossy is None else lossy.data_ptr(), _stream_ptr(stream))
+    _check("nvfp4_fuse_rescale", st)
+    return g_star.value, lossy
+
+
+def nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_dtype=None, out=None, stream=None):
+    """C = A_hat W_hat^T from two quantised operands (K along the last axis)."""
+    torch = _torch()
+    m, kh = a_codes.shape
+    n = w_codes.shape[0]
+    k = kh * 2
+    if w_codes.shape[1] != kh or a_scales.shape != (m, k // 16) or w_scales.shape != (n, k // 16):
+        raise ValueError("operand shapes do not match")
+    for t, nm in ((a_codes, "a_codes"), (a_scales, "a_scales"), (w_codes, "w_codes"), (w_scales, "w_scales")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype or torch.float32, device=a_codes.device)
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != m or out.shape[1] < n:
+        raise ValueError("out must be [m, >=n] with unit column stride")
+    st = load_library().nvfp4_gemm(m, n, k, _dev(a_codes, "a_codes"), _dev(a_scales, "a_scales"),
+                                   _dev(a_gscale, "a_gscale"), _dev(w_codes, "w_codes"), _dev(w_scales, "w_scales"),
+                                   _dev(w_gscale, "w_gscale"), _dev(out, "out"), _dtype_code(out.dtype),
+                                   out.stride(0), _stream_ptr(stream))
+    _check("nvfp4_gemm", st)
+    return out

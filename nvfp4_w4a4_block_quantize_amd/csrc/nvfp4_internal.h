@@ -1,0 +1,29 @@
+// Launchers shared between the C-ABI layer and the kernel translation units.
+// Arguments are validated by the caller (nvfp4_abi.cpp); these only launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Quantiser: dtype 0 = f32, 1 = bf16, 2 = f16.  dynamic != 0 first writes g
+// into *gscale (the word doubles as the amax reduction buffer).
+hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, float* gscale,
+                           bool dynamic, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+// Fold rho = g_star / g_module into `count` scale bytes starting at `scales`;
+// adds the number of changed dequantisation factors to *lossy when non-null.
+hipError_t launch_fuse_rescale(uint8_t* scales, int64_t count, float g_star, float g_module, int64_t* lossy,
+                               hipStream_t stream);
+hipError_t launch_zero_i64(int64_t* p, hipStream_t stream);
+
+// GEMM C = alpha * A_hat W_hat^T; out_dtype 0 = f32, 1 = bf16, 2 = f16.
+hipError_t launch_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
+                       const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
+                       const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace nvfp4

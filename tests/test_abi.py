@@ -1,0 +1,111 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and rejects invalid arguments before touching HIP (a rejected call
+returns its status without any device work, so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_w4a4_block_quantize_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:nvfp4_status|const char\s*\*|int32_t)\s*(nvfp4_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(nv.LIB_PATH):
+        pytest.skip("libnvfp4.so not built")
+    return nv.load_library()
+
+
+def test_header_declares_the_three_operations():
+    fns = declared_functions()
+    for name in ("nvfp4_quantize", "nvfp4_fuse_rescale", "nvfp4_gemm", "nvfp4_status_str", "nvfp4_abi_version"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(nv.SIGNATURES)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.nvfp4_abi_version() == 1
+    for s in range(7):
+        assert len(lib.nvfp4_status_str(s)) > 0
+    assert lib.nvfp4_status_str(99) == b"unknown status"
+
+
+# a fake, 256-byte-aligned "device" address: validation never dereferences it
+P = 1 << 20
+
+
+def q(lib, **kw):
+    a = dict(x=P, x_dtype=1, rows=4, cols=32, ldx=32, gscale=P, mode=0, codes=P, scales=P, stream=None)
+    a.update(kw)
+    return lib.nvfp4_quantize(a["x"], a["x_dtype"], a["rows"], a["cols"], a["ldx"], a["gscale"], a["mode"],
+                              a["codes"], a["scales"], a["stream"])
+
+
+def test_quantize_validation(lib):
+    assert q(lib, x=None) == 1
+    assert q(lib, codes=None) == 1
+    assert q(lib, x_dtype=7) == 4
+    assert q(lib, mode=3) == 4
+    assert q(lib, rows=0) == 2
+    assert q(lib, cols=24) == 2
+    assert q(lib, ldx=16) == 2
+    assert q(lib, cols=-16) == 2
+    assert q(lib, x=P + 8) == 3
+    assert q(lib, x_dtype=1, ldx=36) == 3  # 36 bf16 = 72 bytes, not a multiple of 16
+    assert q(lib, codes=P + 2) == 3
+
+
+def g(lib, **kw):
+    a = dict(m=8, n=8, k=32, ac=P, asc=P, ag=P, wc=P, wsc=P, wg=P, c=P, dt=0, ldc=8)
+    a.update(kw)
+    return lib.nvfp4_gemm(a["m"], a["n"], a["k"], a["ac"], a["asc"], a["ag"], a["wc"], a["wsc"], a["wg"], a["c"],
+                          a["dt"], a["ldc"], None)
+
+
+def test_gemm_validation(lib):
+    assert g(lib, ac=None) == 1
+    assert g(lib, wg=None) == 1
+    assert g(lib, c=None) == 1
+    assert g(lib, dt=5) == 4
+    assert g(lib, m=0) == 2
+    assert g(lib, k=40) == 2
+    assert g(lib, ldc=4) == 2
+    assert g(lib, ac=P + 8) == 3
+    assert g(lib, c=P + 2, dt=0) == 3
+
+
+def f(lib, rows=(4, 4), gs=(1.0, 2.0), k=32, scales=P, out=True):
+    n = len(rows)
+    r = (ctypes.c_int64 * max(n, 1))(*rows)
+    gg = (ctypes.c_float * max(n, 1))(*gs)
+    o = ctypes.c_float(-1.0)
+    st = lib.nvfp4_fuse_rescale(scales, k, n, ctypes.cast(r, ctypes.c_void_p), ctypes.cast(gg, ctypes.c_void_p),
+                                ctypes.addressof(o) if out else None, None, None)
+    return st, o.value
+
+
+def test_fuse_rescale_validation_writes_nothing_on_error(lib):
+    assert f(lib, scales=None) == (1, -1.0)
+    assert f(lib, out=False)[0] == 1
+    assert f(lib, k=24) == (2, -1.0)
+    assert f(lib, rows=(4, 0)) == (2, -1.0)
+    assert f(lib, gs=(1.0, 0.0)) == (5, -1.0)
+    assert f(lib, gs=(1.0, float("inf"))) == (5, -1.0)
+    assert f(lib, gs=(float("nan"), 1.0)) == (5, -1.0)
+    assert f(lib, rows=(), gs=()) == (5, -1.0)
+    assert f(lib, rows=(1,) * 65, gs=(1.0,) * 65) == (5, -1.0)

@@ -1,0 +1,245 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Codes and scale bytes must match bit for bit; the GEMM must satisfy
+|C_gpu - C_ref| <= 1e-5 * sum_k |a_k w_k| per element (fp32 output), with
+bf16 / f16 outputs allowed one extra unit in the last place of the narrow
+type.  Inputs are seeded (nvfp4_w4a4_block_quantize_amd.synth) or
+hand-built edge cases.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from nvfp4_w4a4_block_quantize_amd import synth
+from oracle import nvfp4_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def log(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_f32(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def dev_bf16(x):
+    bits = synth.bf16_bits(x).view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(bits)).cuda().view(torch.bfloat16)
+
+
+def dev_f16(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float16)).cuda()
+
+
+def gscale_tensor(g):
+    return torch.tensor([float(np.float32(g))], dtype=torch.float32, device="cuda")
+
+
+def quantize_gpu(nv, x, dtype, g=None):
+    """x: float32 array holding values of `dtype`; g None = dynamic."""
+    t = {"f32": dev_f32, "bf16": dev_bf16, "f16": dev_f16}[dtype](x)
+    gs = gscale_tensor(0.0 if g is None else g)
+    codes, scales = nv.nvfp4_quantize(t, gs, "dynamic" if g is None else "static")
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy(), np.float32(gs.cpu().numpy()[0])
+
+
+def assert_quant_equal(nv, x, dtype, g=None, label=""):
+    log("quantize", label, dtype, x.shape, "dynamic" if g is None else f"g={g}")
+    c, s, gg = quantize_gpu(nv, x, dtype, g)
+    rc, rs, rg = O.quantize_ref(x, g)
+    assert gg == rg, (gg, rg)
+    assert np.array_equal(s, rs), f"scale mismatch at {np.argwhere(s != rs)[:5]}"
+    assert np.array_equal(c, rc), f"code mismatch at {np.argwhere(c != rc)[:5]}"
+
+
+# ------------------------------------------------------------------ quantiser
+def test_quantize_tiny_fp32_dynamic(gpu_lib):
+    (lin,) = synth.make_workload("tiny")
+    assert_quant_equal(gpu_lib, lin.a, "f32", None, "tiny A")
+    assert_quant_equal(gpu_lib, lin.modules[0][1], "f32", None, "tiny W")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_quantize_random_static_and_dynamic(gpu_lib, dtype):
+    rng = np.random.default_rng(21)
+    for rows, cols in ((1, 16), (3, 48), (37, 272), (129, 1040)):
+        x = (rng.standard_t(3, (rows, cols)) * 2).astype(np.float32)
+        x[:, rng.integers(0, cols)] *= 50
+        x = synth.round_to_bf16(x) if dtype == "bf16" else (np.clip(x, -6e4, 6e4).astype(np.float16).astype(np.float32) if dtype == "f16" else x)
+        assert_quant_equal(gpu_lib, x, dtype, None, f"random {rows}x{cols}")
+        assert_quant_equal(gpu_lib, x, dtype, np.float32(37.5), f"random {rows}x{cols}")
+
+
+def test_quantize_adversarial_blocks(gpu_lib):
+    """Ties of E2M1 after scaling, zero blocks, underflowing blocks, static-g
+    saturation and negative zeros."""
+    g = np.float32(1.0)
+    grid = np.array([0, 0.25, 0.5, 0.75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6, 6], np.float32)
+    rows = [grid, -grid, np.zeros(16, np.float32), np.full(16, -0.0, np.float32),
+            np.array([1e-30] + [0] * 15, np.float32), np.array([100, -80, 3, 0.1] + [0] * 12, np.float32),
+            np.nextafter(grid, np.float32(10)), np.nextafter(grid, np.float32(-10))]
+    x = np.stack(rows).astype(np.float32)
+    x[:, -1] = 6.0  # block amax 6 so that scale = 1 and y = x exactly
+    assert_quant_equal(gpu_lib, x, "f32", g, "ties and edges")
+    assert_quant_equal(gpu_lib, x, "f32", np.float32(1e-7), "underflow")
+    assert_quant_equal(gpu_lib, x, "f32", np.float32(1e4), "saturation")
+    assert_quant_equal(gpu_lib, x, "f32", None, "dynamic")
+    assert_quant_equal(gpu_lib, np.zeros((4, 64), np.float32), "f32", None, "all zero")
+
+
+def test_quantize_strided_rows(gpu_lib):
+    rng = np.random.default_rng(22)
+    x = synth.round_to_bf16(rng.standard_normal((20, 96)).astype(np.float32))
+    full = np.zeros((20, 128), np.float32)
+    full[:, :96] = x
+    t = dev_bf16(full)[:, :96]
+    gs = gscale_tensor(0)
+    codes, scales = gpu_lib.nvfp4_quantize(t, gs, "dynamic")
+    rc, rs, rg = O.quantize_ref(x)
+    assert np.array_equal(codes.cpu().numpy(), rc) and np.array_equal(scales.cpu().numpy(), rs)
+    assert np.float32(gs.item()) == rg
+
+
+def test_quantize_deterministic(gpu_lib):
+    rng = np.random.default_rng(23)
+    x = synth.round_to_bf16(rng.standard_normal((512, 5120)).astype(np.float32))
+    a = quantize_gpu(gpu_lib, x, "bf16", None)
+    b = quantize_gpu(gpu_lib, x, "bf16", None)
+    assert all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
+# ------------------------------------------------------------------ fuse-rescale
+def test_fuse_rescale_matches_oracle(gpu_lib):
+    rng = np.random.default_rng(24)
+    rows = [96, 64, 3, 5]
+    K = 256
+    qs = []
+    for i, r in enumerate(rows):
+        w = (rng.standard_normal((r, K)) * [0.021, 0.017, 0.005, 0.09][i]).astype(np.float32)
+        qs.append(quantize_gpu(gpu_lib, synth.round_to_bf16(w), "bf16", None))
+    scales = np.concatenate([q[1] for q in qs])
+    gs = [q[2] for q in qs]
+    log("fuse", rows, gs)
+    t = torch.from_numpy(scales.copy()).cuda()
+    g_star, lossy = gpu_lib.nvfp4_fuse_rescale(t, K, rows, gs)
+    torch.cuda.synchronize()
+    ref, ref_g, ref_lossy = O.fuse_rescale_ref(scales, rows, gs)
+    assert np.float32(g_star) == ref_g
+    assert np.array_equal(t.cpu().numpy(), ref)
+    assert int(lossy.item()) == ref_lossy
+
+
+def test_fuse_rescale_single_module_is_identity(gpu_lib):
+    s = np.random.default_rng(25).integers(0, 0x7F, (7, 4)).astype(np.uint8)
+    t = torch.from_numpy(s.copy()).cuda()
+    g, lossy = gpu_lib.nvfp4_fuse_rescale(t, 64, [7], [3.0])
+    torch.cuda.synchronize()
+    assert g == 3.0 and np.array_equal(t.cpu().numpy(), s) and int(lossy.item()) == 0
+
+
+# ------------------------------------------------------------------ GEMM
+def rand_operand(rng, rows, K, scale_lo=0x20, scale_hi=0x58):
+    codes = rng.integers(0, 256, (rows, K // 2)).astype(np.uint8)
+    scales = rng.integers(scale_lo, scale_hi, (rows, K // 16)).astype(np.uint8)
+    return codes, scales
+
+
+def gemm_gpu(nv, ac, asc, ga, wc, wsc, gw, out_dtype):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    c = nv.nvfp4_gemm(t(ac), t(asc), gscale_tensor(ga), t(wc), t(wsc), gscale_tensor(gw),
+                      out_dtype={"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[out_dtype])
+    torch.cuda.synchronize()
+    return c.float().cpu().numpy()
+
+
+def check_gemm(C, ref, bound, out_dtype):
+    err = np.abs(C.astype(np.float64) - ref)
+    lim = 1e-5 * bound
+    if out_dtype == "bf16":
+        lim = lim + 2.0 ** -8 * np.abs(ref)
+    elif out_dtype == "f16":
+        lim = lim + 2.0 ** -11 * np.abs(ref) + 2.0 ** -24
+    bad = err > lim
+    assert not bad.any(), f"{int(bad.sum())} elements out of tolerance, worst at {np.argwhere(bad)[:3]}, " \
+                          f"err {err[bad][:3]}, lim {lim[bad][:3]}"
+    zero_rows = bound == 0
+    assert np.all(C[zero_rows] == 0)
+
+
+@pytest.mark.parametrize("shape", [(64, 128, 256), (300, 520, 384), (1, 1, 16), (33, 257, 400), (256, 256, 128),
+                                   (513, 300, 1056), (32, 1000, 640), (7, 333, 48), (64, 96, 4096)])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_gemm_random_codes(gpu_lib, shape, out_dtype):
+    M, N, K = shape
+    rng = np.random.default_rng([26, M, N, K])
+    ac, asc = rand_operand(rng, M, K)
+    wc, wsc = rand_operand(rng, N, K)
+    ga, gw = np.float32(rng.uniform(0.5, 300)), np.float32(rng.uniform(100, 3e4))
+    log("gemm", shape, out_dtype)
+    C = gemm_gpu(gpu_lib, ac, asc, ga, wc, wsc, gw, out_dtype)
+    ref, bound = O.gemm_ref(ac, asc, ga, wc, wsc, gw)
+    check_gemm(C, ref, bound, out_dtype)
+
+
+def test_gemm_f16_output(gpu_lib):
+    rng = np.random.default_rng(27)
+    ac, asc = rand_operand(rng, 70, 512, 0x30, 0x40)
+    wc, wsc = rand_operand(rng, 90, 512, 0x30, 0x40)
+    C = gemm_gpu(gpu_lib, ac, asc, np.float32(64), wc, wsc, np.float32(64), "f16")
+    ref, bound = O.gemm_ref(ac, asc, np.float32(64), wc, wsc, np.float32(64))
+    check_gemm(C, ref, bound, "f16")
+
+
+def test_gemm_extreme_scales(gpu_lib):
+    """Smallest and largest decoded magnitudes (E4M3 subnormal 2^-9 and 448 with
+    codes 0.5 and 6) stay exact through the fp16 decode."""
+    K = 256
+    for sc in (0x01, 0x07, 0x08, 0x7E):
+        ac = np.full((40, K // 2), 0x71, np.uint8)  # elements 0.5, 6, 0.5, 6, ...
+        asc = np.full((40, K // 16), sc, np.uint8)
+        wc = np.full((50, K // 2), 0x9F, np.uint8)  # -6, -0.5, ...
+        wsc = np.full((50, K // 16), 0x38, np.uint8)
+        C = gemm_gpu(gpu_lib, ac, asc, np.float32(1), wc, wsc, np.float32(1), "f32")
+        ref, bound = O.gemm_ref(ac, asc, np.float32(1), wc, wsc, np.float32(1))
+        assert np.array_equal(C.astype(np.float64), ref), sc
+
+
+def test_gemm_zero_operand_gives_exact_zeros(gpu_lib):
+    rng = np.random.default_rng(28)
+    ac = np.zeros((65, 128), np.uint8)
+    asc = rng.integers(0, 0x7F, (65, 16)).astype(np.uint8)
+    wc, wsc = rand_operand(rng, 70, 256)
+    C = gemm_gpu(gpu_lib, ac, asc, np.float32(1), wc, wsc, np.float32(1), "f32")
+    assert np.all(C == 0)
+
+
+def test_gemm_deterministic(gpu_lib):
+    rng = np.random.default_rng(29)
+    ac, asc = rand_operand(rng, 300, 1024)
+    wc, wsc = rand_operand(rng, 600, 1024)
+    a = gemm_gpu(gpu_lib, ac, asc, np.float32(3), wc, wsc, np.float32(5), "f32")
+    b = gemm_gpu(gpu_lib, ac, asc, np.float32(3), wc, wsc, np.float32(5), "f32")
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ end to end, tiny workload
+def test_tiny_end_to_end(gpu_lib):
+    (lin,) = synth.make_workload("tiny")
+    a, w = lin.a, lin.modules[0][1]
+    ga_t = gscale_tensor(0)
+    gw_t = gscale_tensor(0)
+    ac, asc = gpu_lib.nvfp4_quantize(dev_f32(a), ga_t, "dynamic")
+    wc, wsc = gpu_lib.nvfp4_quantize(dev_f32(w), gw_t, "dynamic")
+    C = gpu_lib.nvfp4_gemm(ac, asc, ga_t, wc, wsc, gw_t, torch.float32).cpu().numpy()
+    rac, rasc, rga = O.quantize_ref(a)
+    rwc, rwsc, rgw = O.quantize_ref(w)
+    assert np.array_equal(ac.cpu().numpy(), rac) and np.array_equal(wc.cpu().numpy(), rwc)
+    ref, bound = O.gemm_ref(rac, rasc, rga, rwc, rwsc, rgw)
+    check_gemm(C, ref, bound, "f32")
