@@ -1,0 +1,273 @@
+"""Throughput of the NVFP4 W4A4 linear layer on one MI355X.
+
+One step = the whole hot path over one batch: online quantisation of the
+activations (static, calibrated global scale) followed by the block-scaled
+W4A4 GEMM against pre-quantised, fuse-rescaled weights (weight preparation is
+offline, as on the pages, and not timed).  Default workload: the GDN fused
+input projection at 8K-token prefill, A[8192x5120] bf16 -> W[14432x5120]
+(qkv 8192 + z 6144 + a 48 + b 48, four modules calibrated separately and
+fused by global-scale repair), bf16 output.
+
+Prints one JSON line.  `value` is whole-step TFLOP/s = 2*M*N*K / step time
+(quantisation included); `roofline` covers the dominant kernel (the GEMM),
+timed with HIP events on the stream it runs on; `cpu_baseline` times the CPU
+oracle on a bounded row sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload gdn|mlp|decode|long]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A4 GEMM TFLOP/s incl. act-quant at 8K-token prefill; % of MFMA/HBM roofline"
+PEAK_F16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+GEMM_SRCS = [os.path.join(ROOT, "nvfp4_w4a4_block_quantize_amd", "csrc", f)
+             for f in ("gemm.hip", "gemm_fast.hip", "gemm_common.h", "nvfp4_device.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="gdn", choices=["gdn", "mlp", "decode", "long"])
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=8192, help="activation rows in the oracle's timed sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain device copy of known size (for HBM counter scaling)")
+    return p.parse_args()
+
+
+def gemm_source_sha():
+    h = hashlib.sha256()
+    for p in GEMM_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per GEMM launch from committed rocprofv3 counters, valid only
+    for the GEMM source they were taken on."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = d.get(workload)
+    if not e or e.get("gemm_source_sha") != gemm_source_sha():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+class Prepared:
+    """Device-resident operands of one GEMM of the workload."""
+
+    def __init__(self, nv, torch, lin, rotate=1):
+        dev = torch.device("cuda:0")
+        self.m, self.k = lin.a.shape
+        self.n = lin.n
+        to_dev = (lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)) if lin.a_dtype == "f32" \
+            else (lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev).to(torch.bfloat16))
+        self.a = to_dev(lin.a)
+        # static activation scale: calibrated on a separate draw of the same distribution
+        self.ga = torch.zeros(1, dtype=torch.float32, device=dev)
+        nv.nvfp4_quantize(to_dev(lin.a_calib), self.ga, "dynamic")
+        # weights: each module quantised with its own dynamic scale into its rows of one buffer
+        self.wc = torch.empty((self.n, self.k // 2), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty((self.n, self.k // 16), dtype=torch.uint8, device=dev)
+        gs, rows, r0 = [], [], 0
+        for _, w in lin.modules:
+            g = torch.zeros(1, dtype=torch.float32, device=dev)
+            nv.nvfp4_quantize(to_dev(w), g, "dynamic", codes=self.wc[r0:r0 + w.shape[0]],
+                              scales=self.ws[r0:r0 + w.shape[0]])
+            gs.append(float(g.item()))
+            rows.append(w.shape[0])
+            r0 += w.shape[0]
+        g_star, self.lossy = nv.nvfp4_fuse_rescale(self.ws, self.k, rows, gs) if len(rows) > 1 else (gs[0], None)
+        self.gw = torch.tensor([g_star], dtype=torch.float32, device=dev)
+        self.module_gscales = gs
+        self.module_rows = rows
+        self.copies = [(self.wc, self.ws)] + [(self.wc.clone(), self.ws.clone()) for _ in range(rotate - 1)]
+        self.ac = torch.empty((self.m, self.k // 2), dtype=torch.uint8, device=dev)
+        self.asc = torch.empty((self.m, self.k // 16), dtype=torch.uint8, device=dev)
+        self.c = torch.empty((self.m, self.n), dtype=torch.bfloat16, device=dev)
+
+    def flops(self):
+        return 2.0 * self.m * self.n * self.k
+
+    def gemm_bytes(self):
+        """Algorithmic HBM bytes of one GEMM: both operands' codes + scales once, C once."""
+        return (self.m + self.n) * (self.k // 2 + self.k // 16) + self.m * self.n * 2
+
+    def quant_bytes(self):
+        return self.m * self.k * self.a.element_size() + self.m * (self.k // 2 + self.k // 16)
+
+
+def run(args):
+    import torch
+
+    import nvfp4_w4a4_block_quantize_amd as nv
+    from nvfp4_w4a4_block_quantize_amd import synth
+
+    nv.load_library()
+    torch.cuda.init()
+    lins = synth.make_workload(args.workload, seed=args.seed)
+    rotate = 4 if args.workload == "decode" else 1
+    preps = [Prepared(nv, torch, lin, rotate=rotate) for lin in lins]
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        for j, p in enumerate(preps):
+            wc, ws = p.copies[i % len(p.copies)]
+            if ev is not None:
+                ev[j][0].record()
+            nv.nvfp4_quantize(p.a, p.ga, "static", codes=p.ac, scales=p.asc)
+            if ev is not None:
+                ev[j][1].record()
+            nv.nvfp4_gemm(p.ac, p.asc, p.ga, wc, ws, p.gw, out=p.c)
+            if ev is not None:
+                ev[j][2].record()
+
+    steps = args.steps if args.workload != "decode" else max(args.steps, 1000)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region 1: the whole step, back to back (this is `value`)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+
+    # timed region 2: the same steps with events between the kernels (per-kernel durations)
+    n_ev = min(steps, 200)
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in preps] for _ in range(n_ev)]
+    torch.cuda.synchronize()
+    for i in range(n_ev):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    q_ms = [float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(n_ev)])) for j in range(len(preps))]
+    g_ms = [float(np.mean([evs[i][j][1].elapsed_time(evs[i][j][2]) for i in range(n_ev)])) for j in range(len(preps))]
+
+    flops = sum(p.flops() for p in preps)
+    if args.workload == "decode":
+        p = preps[0]
+        step_bytes = p.gemm_bytes() + p.quant_bytes() + p.m * (p.k // 2 + p.k // 16)
+        value, unit = step_bytes / (ms_step * 1e-3) / 1e9, "GB/s"
+        gb = p.gemm_bytes() / (g_ms[0] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gb, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gb / PEAK_HBM_GBS, 4), "traffic": load_traffic(args.workload),
+                "kernel": "nvfp4 gemm (decode shape)", "avg_ms": round(g_ms[0], 5)}
+        metric = "W4A4 decode-shaped GEMM GB/s incl. act-quant (M=32), % of HBM roofline"
+    else:
+        value, unit = flops / (ms_step * 1e-3) / 1e12, "TFLOP/s"
+        # dominant kernel: the largest GEMM of the step
+        j = int(np.argmax([p.flops() for p in preps]))
+        ach = preps[j].flops() / (g_ms[j] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_F16_MFMA_TFLOPS, 4), "traffic": load_traffic(args.workload),
+                "kernel": f"nvfp4 gemm {preps[j].m}x{preps[j].n}x{preps[j].k}", "avg_ms": round(g_ms[j], 5)}
+        metric = METRIC
+
+    out = {
+        "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "e2m1xe2m1 decoded exactly to f16, f16 MFMA, f32 accumulate",
+        "data": "synthetic (seeded; no dataset or trained weights)",
+        "config": {
+            "workload": {"gdn": "gdn_fused_in_proj_prefill_8k", "mlp": "mlp_gate_up_down_prefill_8k",
+                         "decode": "decode_gate_up_m32", "long": "attn_qkv_o_prefill_32k"}[args.workload],
+            "gemms": [{"name": lin.name, "M": p.m, "N": p.n, "K": p.k, "modules": p.module_rows,
+                       "quant_ms": round(q, 5), "gemm_ms": round(g, 5),
+                       "gemm_tflops": round(p.flops() / (g * 1e-3) / 1e12, 2),
+                       "quant_gbs": round(p.quant_bytes() / (q * 1e-3) / 1e9, 1)}
+                      for lin, p, q, g in zip(lins, preps, q_ms, g_ms)],
+            "a_dtype": lins[0].a_dtype, "c_dtype": "bf16", "act_gscale": "static (calibrated on a separate draw)",
+            "weights": "pre-quantised per module, fuse-rescaled, not timed",
+            "weight_copies_rotated": rotate, "gemm_source_sha": gemm_source_sha(),
+        },
+        "roofline": roof,
+    }
+    if args.copy_calibration:
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = nbytes
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(lins, args.cpu_rows, args.workload)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(lins, rows, workload):
+    """The oracle, as it stands, on a bounded row sample of the same workload:
+    quantise `rows` activation rows and multiply them (float64) against the
+    oracle's own quantised, fuse-rescaled weights.  Weight preparation is not
+    timed, as on the GPU side."""
+    from oracle import nvfp4_oracle as O
+
+    lin = max(lins, key=lambda l: l.m * l.n * l.k)
+    rows = min(rows, lin.m)
+    a = lin.a[:rows]
+    _, _, g_a = O.quantize_ref(lin.a_calib)
+    qs = [O.quantize_ref(w) for _, w in lin.modules]
+    wc = np.concatenate([q[0] for q in qs])
+    if len(qs) > 1:
+        ws, g_w, _ = O.fuse_rescale_ref(np.concatenate([q[1] for q in qs]), [q[0].shape[0] for q in qs],
+                                        [q[2] for q in qs])
+    else:
+        ws, g_w = qs[0][1], qs[0][2]
+    t0 = time.perf_counter()
+    ac, asc, _ = O.quantize_ref(a, g_a)
+    O.gemm_ref(ac, asc, g_a, wc, ws, g_w)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * lin.n * lin.k
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    if workload == "decode":
+        byts = rows * lin.k * 2 + lin.n * (lin.k // 2 + lin.k // 16)
+        return {"value": round(byts / dt / 1e9, 4), "unit": "GB/s", "cores": min(cores, threads), "kind": "oracle",
+                "seconds": round(dt, 2),
+                "sample": f"{rows} of {lin.m} rows of {lin.name}: quantise + float64 dequantise-matmul vs full W"}
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": min(cores, threads), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"{rows} of {lin.m} activation rows of {lin.name} (N={lin.n}, K={lin.k}): quantise + "
+                      f"float64 dequantise-matmul (plus its |a||w| bound) against the full weight"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}), flush=True)
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -31,29 +31,13 @@
 //    (row >> 1) & 3, so 8 lanes reading 8 consecutive rows hit 8 distinct
 //    16-byte bank groups; scale words are stored [half][row] so a wave reads
 //    128 contiguous bytes per half.
-#include <type_traits>
-
-#include "nvfp4_device.h"
+#include "gemm_common.h"
 #include "nvfp4_internal.h"
 
 namespace nvfp4 {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBK = 128;                // K elements per stage
-constexpr int kRowBytes = kBK / 2;      // code bytes per row per stage
-constexpr int kBlocksPerStage = kBK / 16;
-
-template <int BM, int BN>
-struct Layout {
-  static constexpr int a_codes = 0;
-  static constexpr int w_codes = a_codes + BM * kRowBytes;
-  static constexpr int a_scales = w_codes + BN * kRowBytes;  // [2][BM] words
-  static constexpr int w_scales = a_scales + BM * kBlocksPerStage;
-  static constexpr int stage_bytes = w_scales + BN * kBlocksPerStage;
-};
-
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+using namespace gemm;
 
 // ---------------------------------------------------------------- global -> LDS
 // FAST: k % 128 == 0, codes 16-byte aligned rows (k % 32 == 0 follows), scale
@@ -153,37 +137,6 @@ struct GenericLoader {
     }
   }
 };
-
-// ---------------------------------------------------------------- decode
-__device__ __forceinline__ half8_t decode8(uint32_t codes, half2_t s) {
-  half2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
-  half2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
-  half2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2);
-  half2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3);
-  v0 *= s;
-  v1 *= s;
-  v2 *= s;
-  v3 *= s;
-  half8_t r;
-  r[0] = v0[0]; r[1] = v0[1]; r[2] = v1[0]; r[3] = v1[1];
-  r[4] = v2[0]; r[5] = v2[1]; r[6] = v3[0]; r[7] = v3[1];
-  return r;
-}
-
-// Four E4M3 scale bytes -> four fp16 pairs (S_q, S_q), exact.
-__device__ __forceinline__ void scale_pairs(uint32_t w, half2_t (&p)[4]) {
-  const uint32_t lo = __builtin_amdgcn_perm(w, w, 0x01010000u);  // b0 b0 b1 b1
-  const uint32_t hi = __builtin_amdgcn_perm(w, w, 0x03030202u);  // b2 b2 b3 b3
-  p[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
-  p[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
-  p[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
-  p[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
-}
-
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
 
 // ---------------------------------------------------------------- kernel
 template <int BM, int BN, int WM, int WN, bool FAST, int OUT>
@@ -336,6 +289,9 @@ hipError_t launch_cfg(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, c
 hipError_t launch_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                        const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
                        const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream) {
+  if (gemm_fast_supported(m, n, k, a_codes, a_scales, w_codes, w_scales))
+    return launch_gemm_fast(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype, ldc,
+                            stream);
   const bool fast = (k % kBK) == 0 && (reinterpret_cast<uintptr_t>(a_codes) % 16) == 0 &&
                     (reinterpret_cast<uintptr_t>(w_codes) % 16) == 0 &&
                     (reinterpret_cast<uintptr_t>(a_scales) % 8) == 0 &&

@@ -1,0 +1,74 @@
+// Shared pieces of the two GEMM paths: the per-stage LDS layout, the
+// fragment decode (E2M1 codes x E4M3 block scale -> exact fp16) and output
+// conversion.  Included by gemm.hip and gemm_fast.hip only.
+#pragma once
+
+#include <type_traits>
+
+#include "nvfp4_device.h"
+
+namespace nvfp4 {
+namespace gemm {
+
+constexpr int kThreads = 256;
+constexpr int kBK = 128;                // K elements per stage
+constexpr int kRowBytes = kBK / 2;      // code bytes per row per stage
+constexpr int kBlocksPerStage = kBK / 16;
+
+template <int BM, int BN>
+struct Layout {
+  static constexpr int a_codes = 0;
+  static constexpr int w_codes = a_codes + BM * kRowBytes;
+  static constexpr int a_scales = w_codes + BN * kRowBytes;  // [2][BM] words
+  static constexpr int w_scales = a_scales + BM * kBlocksPerStage;
+  static constexpr int stage_bytes = w_scales + BN * kBlocksPerStage;
+};
+
+// 16-byte chunk swizzle of a 64-byte LDS code row: 8 consecutive rows read at
+// the same logical chunk land in 8 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+
+// Eight codes (one 32-bit word) times one block scale -> eight exact fp16 values.
+__device__ __forceinline__ half8_t decode8(uint32_t codes, half2_t s) {
+  half2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
+  half2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
+  half2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2);
+  half2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3);
+  v0 *= s;
+  v1 *= s;
+  v2 *= s;
+  v3 *= s;
+  half8_t r;
+  r[0] = v0[0]; r[1] = v0[1]; r[2] = v1[0]; r[3] = v1[1];
+  r[4] = v2[0]; r[5] = v2[1]; r[6] = v3[0]; r[7] = v3[1];
+  return r;
+}
+
+// Four E4M3 scale bytes -> four fp16 pairs (S_q, S_q), exact.
+__device__ __forceinline__ void scale_pairs(uint32_t w, half2_t (&p)[4]) {
+  const uint32_t lo = __builtin_amdgcn_perm(w, w, 0x01010000u);  // b0 b0 b1 b1
+  const uint32_t hi = __builtin_amdgcn_perm(w, w, 0x03030202u);  // b2 b2 b3 b3
+  p[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  p[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  p[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  p[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+}
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int OUT>
+__device__ __forceinline__ void store_out(void* c, int64_t idx, float v) {
+  if constexpr (OUT == 0) {
+    static_cast<float*>(c)[idx] = v;
+  } else if constexpr (OUT == 1) {
+    static_cast<uint16_t*>(c)[idx] = (uint16_t)bf16_rne_bits(v);
+  } else {
+    static_cast<_Float16*>(c)[idx] = (_Float16)v;
+  }
+}
+
+}  // namespace gemm
+}  // namespace nvfp4

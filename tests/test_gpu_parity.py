@@ -173,8 +173,13 @@ def check_gemm(C, ref, bound, out_dtype):
     assert np.all(C[zero_rows] == 0)
 
 
-@pytest.mark.parametrize("shape", [(64, 128, 256), (300, 520, 384), (1, 1, 16), (33, 257, 400), (256, 256, 128),
-                                   (513, 300, 1056), (32, 1000, 640), (7, 333, 48), (64, 96, 4096)])
+# shapes with k % 256 == 0 and m > 64 take the main (direct-to-LDS) path; the rest the generic one
+GEMM_SHAPES = [(64, 128, 256), (300, 520, 384), (1, 1, 16), (33, 257, 400), (256, 256, 128), (513, 300, 1056),
+               (32, 1000, 640), (7, 333, 48), (64, 96, 4096),
+               (65, 64, 256), (300, 520, 512), (513, 777, 1024), (257, 300, 256), (1000, 1000, 2560), (256, 512, 5120)]
+
+
+@pytest.mark.parametrize("shape", GEMM_SHAPES)
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_gemm_random_codes(gpu_lib, shape, out_dtype):
     M, N, K = shape
