@@ -24,9 +24,11 @@ struct Layout {
   static constexpr int stage_bytes = w_scales + BN * kBlocksPerStage;
 };
 
-// 16-byte chunk swizzle of a 64-byte LDS code row: 8 consecutive rows read at
-// the same logical chunk land in 8 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+// 16-byte chunk swizzle of a 64-byte LDS code row.  Lanes reading the same
+// logical chunk of consecutive rows hit distinct 16-byte bank groups both when
+// the LDS serves 8 lanes of a 16-byte read per cycle (8 aligned rows over
+// 128 B) and when it serves 16 (16 rows over 256 B).
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
 
 // Eight codes (one 32-bit word) times one block scale -> eight exact fp16 values.
 __device__ __forceinline__ half8_t decode8(uint32_t codes, half2_t s) {

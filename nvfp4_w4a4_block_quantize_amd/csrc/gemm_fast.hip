@@ -1,7 +1,7 @@
 // Main GEMM path for gfx950: C = alpha * A_hat W_hat^T on NVFP4 operands
 // (news article "Qwen3.8-27B最激进4bit量化开源，权重显存暴降2.9倍！", section 02:
 // the W4A4 product of E2M1 codes with E4M3 scales per 16 elements and an FP32
-// global scale per tensor), for k % 256 == 0.
+// global scale per tensor), for k % 512 == 0.
 //
 // Tile: 256 x 256 per workgroup of 4 waves (2 x 2), 128 x 128 per wave = 4 x 4
 // MFMA 32x32x16 tiles, 256 FP32 accumulators per lane.  One stage = 128 K
@@ -13,18 +13,20 @@
 // belongs at its slot; this produces the swizzled code rows and the
 // [half][row] scale words without staging registers.  Two LDS buffers; the
 // fragments of a stage (32 code bytes + one scale word per row and lane half)
-// are double-buffered in registers, so a stage's LDS buffer is free as soon as
-// its fragments have been read.
+// are double-buffered in registers; four LDS stage buffers (separate objects,
+// so the compiler never waits on a direct load into one before reading
+// another) keep the loads of stage kt+3 in flight while stage kt runs.
 //
 // Per stage kt (fragments of kt already in registers, step 0 decoded):
-//   steps 0-3: MFMAs of step s, interleaved with the decode of step s+1;
+//   steps 0-1: MFMAs of step s, interleaved with the decode of step s+1;
 //   wait for this wave's loads of stage kt+1, one workgroup barrier;
-//   step 4: MFMAs interleaved with the LDS reads of stage kt+1's fragments and
-//           the global loads of stage kt+2 (into buffer kt%2);
-//   steps 5-7: as 0-3; step 7 decodes step 0 of stage kt+1.
+//   steps 2-3: also the global loads of stage kt+3 (every other slot);
+//   steps 2-5: also the LDS reads of stage kt+1's fragments (two per step);
+//   steps 6-7: as 0-1; step 7 decodes step 0 of stage kt+1.
 // Interleaving is fixed in source: every MFMA is followed by half a fragment's
-// decode (2 x v_cvt_scalef32_pk_f16_fp4 + 2 x v_pk_mul_f16) and a scheduling
-// fence, which keeps the VALU work under the MFMA shadow.
+// decode (two v_cvt_scalef32_pk_f16_fp4 for this chunk, two v_pk_mul_f16 for
+// the previous chunk, so no multiply waits on the conversion just issued) and
+// a scheduling fence, which keeps the VALU work under the MFMA shadow.
 #include "gemm_common.h"
 #include "nvfp4_internal.h"
 
@@ -41,13 +43,24 @@ typedef __attribute__((address_space(3))) void* lds_void_t;
 
 #if defined(__HIP_DEVICE_COMPILE__)
 
+// s_waitcnt vmcnt(N) with the LDS and export counters unconstrained; the
+// 6-bit vmcnt field is split over bits 3:0 and 15:14
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // vmcnt(N); lgkm and exp counters unconstrained
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
 }
 
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Workgroup barrier ordering LDS only.  Direct-to-LDS loads are ordered by the
+// explicit vmcnt wait before it, so the still-outstanding loads of later stages
+// need not drain (a full __syncthreads() would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 template <int ROWS>
 struct DirectLoader {
@@ -104,36 +117,19 @@ __device__ __forceinline__ uint32_t word_of(const uint4 (&q)[2], int s) {
   return (s & 3) == 0 ? v.x : (s & 3) == 1 ? v.y : (s & 3) == 2 ? v.z : v.w;
 }
 
-// (S_q, S_q) as fp16 for block q (0..3) of a scale word
-__device__ __forceinline__ half2_t scale_pair(uint32_t w, int q) {
-  const uint32_t dup = __builtin_amdgcn_perm(w, w, 0x0C0C0000u | (uint32_t)(q * 0x0101));
-  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(dup, 1.0f, false);
-}
-
-// elements 4*HALF .. 4*HALF+3 of a fragment
-template <int HALF>
-__device__ __forceinline__ void decode_half(uint32_t word, half2_t pair, half8_t& dst) {
-  const half2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2 * HALF) * pair;
-  const half2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2 * HALF + 1) * pair;
-  dst[4 * HALF + 0] = v0[0];
-  dst[4 * HALF + 1] = v0[1];
-  dst[4 * HALF + 2] = v1[0];
-  dst[4 * HALF + 3] = v1[1];
-}
-
 struct Tile {
   DirectLoader<BM> la;
   DirectLoader<BN> lw;
-  lds_ptr_t lds;
-  const uint8_t* smem;
   int wave, wm, wn, lr, h;
   float16_t acc[FM][FN];
-  half8_t fa[FM], fw[FN];  // decoded operands of the current step
-  half8_t ga[FM], gw[FN];  // decoded operands of the next step
-  half2_t pa[FM], pw[FN];  // block-scale pairs for the next step
+  // decoded operands by step parity: F[p][0..3] = A fragments, F[p][4..7] = W
+  half8_t F[2][FM + FN];
+  // fp16 block-scale pairs (S_2b, S_2b+1) of the half stage being decoded
+  half2_t SP[FM + FN];
+  // converted-but-unscaled codes, double-buffered by chunk parity
+  half2_t T[2][2];
 
-  __device__ __forceinline__ void issue_all(int kt) {
-    const lds_ptr_t b = lds + (kt & 1) * L::stage_bytes;
+  __device__ __forceinline__ void issue_all(lds_ptr_t b, int kt) {
 #pragma unroll
     for (int i = 0; i < DirectLoader<BM>::kCodeInstr; ++i) la.issue_code(b + L::a_codes, i, kt, wave);
 #pragma unroll
@@ -144,9 +140,8 @@ struct Tile {
     for (int i = 0; i < DirectLoader<BN>::kScaleInstr; ++i) lw.issue_scale(b + L::w_scales, i, kt, wave);
   }
 
-  // the g-th of 12 global loads of stage kt (interleaved issue)
-  __device__ __forceinline__ void issue_one(int kt, int g) {
-    const lds_ptr_t b = lds + (kt & 1) * L::stage_bytes;
+  // the g-th of the stage's global loads (interleaved issue)
+  __device__ __forceinline__ void issue_one(lds_ptr_t b, int kt, int g) {
     constexpr int C = DirectLoader<BM>::kCodeInstr, S = DirectLoader<BM>::kScaleInstr;
     if (g < C) la.issue_code(b + L::a_codes, g, kt, wave);
     else if (g < C + S) la.issue_scale(b + L::a_scales, g - C, kt, wave);
@@ -172,98 +167,118 @@ struct Tile {
     }
   }
 
-  // chunk q (0..15) of the decode of step s of `src` into ga/gw
-  __device__ __forceinline__ void decode_chunk(const Frags& src, int s, int q) {
-    const int f = q >> 1;
-    if (f < FM) {
-      if ((q & 1) == 0) {
-        pa[f] = scale_pair(src.sa[f], s >> 1);
-        decode_half<0>(word_of(src.a[f], s), pa[f], ga[f]);
-      } else {
-        decode_half<1>(word_of(src.a[f], s), pa[f], ga[f]);
-      }
+  // Decode of step s is split in 16 chunks, chunk q = half (q & 1) of fragment
+  // q >> 1.  start(): two code->fp16 conversions into T[q&1] (and, on the
+  // first chunk of a fragment in a half stage, its scale pair).  finish():
+  // the two block-scale multiplies into F[s&1], one chunk later.
+  __device__ __forceinline__ void start(const Frags& src, int s, int q) {
+    const int f = q >> 1, hf = q & 1;
+    const uint32_t word = f < FM ? word_of(src.a[f], s) : word_of(src.w[f - FM], s);
+    if (hf == 0 && (s & 3) == 0) {
+      const uint32_t sw = f < FM ? src.sa[f] : src.sw[f - FM];
+      SP[f] = s >= 4 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true)
+                     : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+    }
+    if (hf == 0) {
+      T[q & 1][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0);
+      T[q & 1][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1);
     } else {
-      const int j = f - FM;
-      if ((q & 1) == 0) {
-        pw[j] = scale_pair(src.sw[j], s >> 1);
-        decode_half<0>(word_of(src.w[j], s), pw[j], gw[j]);
-      } else {
-        decode_half<1>(word_of(src.w[j], s), pw[j], gw[j]);
-      }
+      T[q & 1][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2);
+      T[q & 1][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3);
     }
   }
+  __device__ __forceinline__ void finish(int s, int q) {
+    const int f = q >> 1, hf = q & 1;
+    const _Float16 sv = ((s >> 1) & 1) ? SP[f][1] : SP[f][0];
+    const half2_t pair = {sv, sv};
+    const half2_t v0 = T[q & 1][0] * pair;
+    const half2_t v1 = T[q & 1][1] * pair;
+    half8_t& d = F[s & 1][f];
+    d[4 * hf + 0] = v0[0];
+    d[4 * hf + 1] = v0[1];
+    d[4 * hf + 2] = v1[0];
+    d[4 * hf + 3] = v1[1];
+  }
 
-  __device__ __forceinline__ void mfma(int q) {
+  // acc[i][j] = W fragment j times A fragment i: the MFMA tile's rows are
+  // output columns, so each lane ends with four runs of four consecutive
+  // output columns of one output row (lane l: row i*32 + l%32, columns
+  // j*32 + 8g + 4*(l/32) + 0..3 for g = 0..3)
+  __device__ __forceinline__ void mfma(int s, int q) {
     const int i = q / FN, j = q % FN;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fw[j], acc[i][j], 0, 0, 0);
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F[s & 1][FM + j], F[s & 1][i], acc[i][j], 0, 0, 0);
   }
 
-  __device__ __forceinline__ void advance() {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) fa[i] = ga[i];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) fw[j] = gw[j];
-  }
-
-  // one MFMA step on fa/fw while decoding step s_next of `src` (DECODE) into ga/gw
-  template <bool DECODE>
-  __device__ __forceinline__ void step(const Frags& src, int s_next) {
+  // MFMAs of step s while decoding step s+1 of `src` (as its step s_src).
+  // CARRY: chunk 15 of the previous decode is still to be finished (it is
+  // finished in the first slot; its fragment is first read by the 4th MFMA).
+  template <bool DECODE, bool CARRY>
+  __device__ __forceinline__ void step(int s, const Frags& src, int s_src) {
 #pragma unroll
     for (int q = 0; q < FM * FN; ++q) {
-      mfma(q);
-      if constexpr (DECODE) decode_chunk(src, s_next, q);
-      fence();
-    }
-    advance();
-  }
-
-  // step 4 after the barrier: also read the next stage's fragments and start
-  // the global loads of the stage after it
-  template <bool ISSUE>
-  __device__ __forceinline__ void step_with_loads(const Frags& cur, Frags& nxt, const uint8_t* nxt_st, int kt_issue) {
-#pragma unroll
-    for (int q = 0; q < FM * FN; ++q) {
-      if (q < FM + FN) read_frag(nxt, nxt_st, q);
-      mfma(q);
-      decode_chunk(cur, 5, q);
-      // all fragment reads (q < 8) precede the first load into LDS, so no read
-      // has to wait behind the new loads
-      if constexpr (ISSUE) {
-        if (q >= 8 && 2 * (q - 8) < kLoadsPerStage) issue_one(kt_issue, 2 * (q - 8));
-        if (q >= 8 && 2 * (q - 8) + 1 < kLoadsPerStage) issue_one(kt_issue, 2 * (q - 8) + 1);
+      mfma(s, q);
+      if (CARRY && q == 0) finish(s, 15);
+      if constexpr (DECODE) {
+        if (q > 0) finish(s + 1, q - 1);
+        start(src, s_src, q);
       }
       fence();
     }
-    advance();
   }
 
-  // One stage.  MORE: a next stage exists (read it into `nxt` after the
-  // barrier and decode its step 0 at the end).  ISSUE: also start the global
-  // loads of stage kt+2.
-  template <bool MORE, bool ISSUE>
-  __device__ __forceinline__ void stage(int kt, const Frags& cur, Frags& nxt) {
-    step<true>(cur, 1);
-    step<true>(cur, 2);
-    step<true>(cur, 3);
-    step<true>(cur, 4);
-    if constexpr (MORE) {
-      wait_vmcnt<0>();
-      __syncthreads();
-      step_with_loads<ISSUE>(cur, nxt, smem + ((kt + 1) & 1) * L::stage_bytes, kt + 2);
-    } else {
-      step<true>(cur, 5);
+  // MFMAs of step s (decoding step s+1 of `cur`) plus, after the barrier,
+  // LDS reads of two of the next stage's fragments (three reads every other
+  // slot) and, in steps 2-3, the twelve global loads of stage kt+3 (every
+  // other slot).
+  template <int S>
+  __device__ __forceinline__ void step_io(const Frags& cur, Frags& nxt, const uint8_t* nxt_st, lds_ptr_t load_buf,
+                                          int kt_load) {
+#pragma unroll
+    for (int q = 0; q < FM * FN; ++q) {
+      mfma(S, q);
+      if (q == 0) finish(S, 15);
+      if (q > 0) finish(S + 1, q - 1);
+      start(cur, S + 1, q);
+      if ((q & 7) == 0) read_frag(nxt, nxt_st, 2 * (S - 2) + (q >> 3));
+      if (S <= 3 && (q & 1) == 1 && 8 * (S - 2) + (q >> 1) < kLoadsPerStage) issue_one(load_buf, kt_load, 8 * (S - 2) + (q >> 1));
+      fence();
     }
-    step<true>(cur, 6);
-    step<true>(cur, 7);
-    if constexpr (MORE) {
-      step<true>(nxt, 0);
-    } else {
-      step<false>(nxt, 0);
-    }
+  }
+
+  // One stage; `cur` holds stage kt (step 0 decoded but for chunk 15), stage
+  // kt+1 sits in LDS buffer `rd` once every wave's loads of it have landed,
+  // and `ld` (the buffer of stage kt-1, already consumed into registers) takes
+  // the global loads of stage kt+3.  Loads and reads issued for stages past
+  // the end of K fetch data that is never multiplied.
+  __device__ __forceinline__ void stage(int kt, const Frags& cur, Frags& nxt, const uint8_t* rd, lds_ptr_t ld) {
+    step<true, true>(0, cur, 1);
+    step<true, true>(1, cur, 2);
+    wait_vmcnt<kLoadsPerStage>();  // stage kt+1 landed; stage kt+2 may still be in flight
+    lds_barrier();
+    step_io<2>(cur, nxt, rd, ld, kt + 3);
+    step_io<3>(cur, nxt, rd, ld, kt + 3);
+    step_io<4>(cur, nxt, rd, ld, kt + 3);
+    step_io<5>(cur, nxt, rd, ld, kt + 3);
+    step<true, true>(6, cur, 7);
+    step<true, true>(7, nxt, 0);
   }
 };
 
 #endif  // __HIP_DEVICE_COMPILE__
+
+// two outputs rounded to nearest even bf16 / f16, packed low-first
+template <int OUT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (OUT == 1) {
+    return bf16_rne_bits(a) | (bf16_rne_bits(b) << 16);
+  } else {
+    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+    uint16_t ua, ub;
+    __builtin_memcpy(&ua, &ha, 2);
+    __builtin_memcpy(&ub, &hb, 2);
+    return (uint32_t)ua | ((uint32_t)ub << 16);
+  }
+}
 
 // XCD-aware tile id: consecutive workgroup ids go round-robin over the 8 XCDs;
 // remap so that tiles adjacent in the grouped order share an XCD (and its L2).
@@ -285,7 +300,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64
                                                                 void* __restrict__ c, int64_t ldc, int tiles_m,
                                                                 int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)  // device-only types below; the host pass needs only the launch stub
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * L::stage_bytes];
+  // four stage buffers as separate objects: the compiler can then tell that
+  // a read of one never depends on a direct-to-LDS load into another
+  __shared__ __attribute__((aligned(1024))) uint8_t buf0[L::stage_bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf1[L::stage_bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf2[L::stage_bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf3[L::stage_bytes];
+  const lds_ptr_t l0 = (lds_ptr_t)buf0, l1 = (lds_ptr_t)buf1, l2 = (lds_ptr_t)buf2, l3 = (lds_ptr_t)buf3;
 
   Tile t;
   const int tid = threadIdx.x;
@@ -295,8 +316,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64
   t.wn = t.wave & 1;
   t.lr = lane & 31;
   t.h = lane >> 5;
-  t.lds = (lds_ptr_t)smem;
-  t.smem = smem;
 
   // grouped tile order (8 tile rows walk the N tiles together) on the XCD-remapped id
   const int total = tiles_m * tiles_n;
@@ -317,39 +336,112 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64
     for (int j = 0; j < FN; ++j) t.acc[i][j] = float16_t{};
 
   const int nk = (int)(K / kBK);
-  t.issue_all(0);
-  t.issue_all(1);
-  wait_vmcnt<kLoadsPerStage>();  // stage 0 landed; stage 1 may still be in flight
+  t.issue_all(l0, 0);
+  t.issue_all(l1, 1);
+  t.issue_all(l2, 2);
+  wait_vmcnt<2 * kLoadsPerStage>();  // stage 0 landed
   __syncthreads();
 
   Frags fx, fy;  // the two fragment register sets, used in turn
 #pragma unroll
-  for (int f = 0; f < FM + FN; ++f) t.read_frag(fx, smem, f);
+  for (int f = 0; f < FM + FN; ++f) t.read_frag(fx, buf0, f);
 #pragma unroll
-  for (int q = 0; q < 16; ++q) t.decode_chunk(fx, 0, q);
-  t.advance();
-
-  // nk is even and >= 2: pairs of stages alternate the two register sets
-  for (int kt = 0; kt + 2 < nk; kt += 2) {
-    t.stage<true, true>(kt, fx, fy);
-    t.stage<true, true>(kt + 1, fy, fx);
+  for (int q = 0; q < 16; ++q) {
+    t.start(fx, 0, q);
+    if (q < 15) t.finish(0, q);  // chunk 15 is finished in the first slot of stage 0
   }
-  t.stage<true, false>(nk - 2, fx, fy);
-  t.stage<false, false>(nk - 1, fy, fx);
 
-  // epilogue: alpha applied once, fp32 or RNE-narrowed store
+  // Four stages per iteration (nk % 4 == 0): two register sets x four LDS
+  // buffers, all static.  Stage kt reads stage kt+1 from buffer (kt+1)%4 and
+  // loads stage kt+3 into buffer (kt+3)%4, which held stage kt-1 (already in
+  // every wave's registers by the barrier of stage kt).
+  for (int kt = 0; kt < nk; kt += 4) {
+    t.stage(kt + 0, fx, fy, buf1, l3);
+    t.stage(kt + 1, fy, fx, buf2, l0);
+    t.stage(kt + 2, fx, fy, buf3, l1);
+    t.stage(kt + 3, fy, fx, buf0, l2);
+  }
+  wait_vmcnt<0>();  // loads issued for stages past the end
+
+  // Epilogue: alpha applied once.  16-bit outputs go through LDS (rows of
+  // 128 values + 16 B pad, two passes of 64 rows per wave) so that each lane
+  // stores 16 contiguous bytes and 16 lanes cover a 256-byte row segment;
+  // fp32 output stores each run of four columns directly.
   const float alpha = 1.0f / (*a_gscale * *w_gscale);
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(c) % 16) == 0 && (ldc * (OUT == 0 ? 4 : 2)) % 16 == 0;
+  const int64_t row_base = m0 + t.wm * TM, col_base = n0 + t.wn * TN;
+  if constexpr (OUT == 0) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      const int64_t row = row_base + i * 32 + t.lr;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t col = n0 + t.wn * TN + j * 32 + t.lr;
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + t.wm * TM + i * 32 + 8 * (e >> 2) + 4 * t.h + (e & 3);
-        if (row < M && col < N) store_out<OUT>(c, row * ldc + col, t.acc[i][j][e] * alpha);
-      }
+        for (int g = 0; g < 4; ++g) {
+          const int64_t col = col_base + j * 32 + 8 * g + 4 * t.h;
+          const float4 v = make_float4(t.acc[i][j][4 * g] * alpha, t.acc[i][j][4 * g + 1] * alpha,
+                                       t.acc[i][j][4 * g + 2] * alpha, t.acc[i][j][4 * g + 3] * alpha);
+          if (row < M) {
+            float* p = static_cast<float*>(c) + row * ldc + col;
+            if (col + 3 < N && vec_ok) {
+              *reinterpret_cast<float4*>(p) = v;
+            } else {
+              if (col < N) p[0] = v.x;
+              if (col + 1 < N) p[1] = v.y;
+              if (col + 2 < N) p[2] = v.z;
+              if (col + 3 < N) p[3] = v.w;
+            }
+          }
+        }
     }
+  } else {
+    wait_vmcnt<0>();  // loads issued for stages past the end may still target LDS
+    __syncthreads();  // every wave is done reading the stage buffers
+    constexpr int kPitch = TN * 2 + 16;  // bytes per staged row
+    static_assert(64 * kPitch <= L::stage_bytes, "a wave's staging rows fit in one stage buffer");
+    // each wave stages in a stage buffer of its own (64 rows x kPitch fit in one)
+    uint8_t* const stg = t.wave < 2 ? (t.wave == 0 ? buf0 : buf1) : (t.wave == 2 ? buf2 : buf3);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * half + ii;
+        const int r = ii * 32 + t.lr;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            uint2 w;
+            w.x = pack2<OUT>(t.acc[i][j][4 * g] * alpha, t.acc[i][j][4 * g + 1] * alpha);
+            w.y = pack2<OUT>(t.acc[i][j][4 * g + 2] * alpha, t.acc[i][j][4 * g + 3] * alpha);
+            *reinterpret_cast<uint2*>(stg + r * kPitch + (j * 32 + 8 * g + 4 * t.h) * 2) = w;
+          }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+      __builtin_amdgcn_wave_barrier();
+      // 64 rows x 256 B: lane reads 16 B; 16 lanes per row, 4 rows per pass
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        const int r = p * 4 + (lane >> 4);
+        const int cb = (lane & 15) * 8;  // first of 8 columns
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kPitch + cb * 2);
+        const int64_t row = row_base + half * 64 + r;
+        const int64_t col = col_base + cb;
+        if (row < M) {
+          uint16_t* q = static_cast<uint16_t*>(c) + row * ldc + col;
+          if (col + 7 < N && vec_ok) {
+            *reinterpret_cast<uint4*>(q) = v;
+          } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (col + e < N) q[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
 #endif
 }
 
@@ -363,7 +455,7 @@ bool gemm_fast_supported(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes
                        (reinterpret_cast<uintptr_t>(w_scales) % 4) == 0;
   // buffer offsets are 32-bit: each operand's code bytes must stay below 2^31
   const bool fits = m * (k / 2) < ((int64_t)1 << 31) && n * (k / 2) < ((int64_t)1 << 31);
-  return aligned && fits && k % (2 * kBK) == 0 && m > 64;  // an even number of stages
+  return aligned && fits && k % (4 * kBK) == 0 && m > 64;  // stages in groups of four
 }
 
 hipError_t launch_gemm_fast(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
