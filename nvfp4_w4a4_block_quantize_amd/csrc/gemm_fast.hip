@@ -18,11 +18,11 @@
 // another) keep the loads of stage kt+3 in flight while stage kt runs.
 //
 // Per stage kt (fragments of kt already in registers, step 0 decoded):
-//   steps 0-1: MFMAs of step s, interleaved with the decode of step s+1;
-//   wait for this wave's loads of stage kt+1, one workgroup barrier;
-//   steps 2-3: also the global loads of stage kt+3 (every other slot);
+//   every step: MFMAs of step s interleaved with the decode of step s+1;
+//   steps 0-5: also two of the global loads of stage kt+3 each;
+//   after step 1: wait for this wave's loads of stage kt+1, one barrier;
 //   steps 2-5: also the LDS reads of stage kt+1's fragments (two per step);
-//   steps 6-7: as 0-1; step 7 decodes step 0 of stage kt+1.
+//   step 7 decodes step 0 of stage kt+1.
 // Interleaving is fixed in source: every MFMA is followed by half a fragment's
 // decode (two v_cvt_scalef32_pk_f16_fp4 for this chunk, two v_pk_mul_f16 for
 // the previous chunk, so no multiply waits on the conversion just issued) and
@@ -209,58 +209,50 @@ struct Tile {
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(F[s & 1][FM + j], F[s & 1][i], acc[i][j], 0, 0, 0);
   }
 
-  // MFMAs of step s while decoding step s+1 of `src` (as its step s_src).
-  // CARRY: chunk 15 of the previous decode is still to be finished (it is
-  // finished in the first slot; its fragment is first read by the 4th MFMA).
-  template <bool DECODE, bool CARRY>
-  __device__ __forceinline__ void step(int s, const Frags& src, int s_src) {
-#pragma unroll
-    for (int q = 0; q < FM * FN; ++q) {
-      mfma(s, q);
-      if (CARRY && q == 0) finish(s, 15);
-      if constexpr (DECODE) {
-        if (q > 0) finish(s + 1, q - 1);
-        start(src, s_src, q);
-      }
-      fence();
-    }
-  }
-
-  // MFMAs of step s (decoding step s+1 of `cur`) plus, after the barrier,
-  // LDS reads of two of the next stage's fragments (three reads every other
-  // slot) and, in steps 2-3, the twelve global loads of stage kt+3 (every
-  // other slot).
+  // Step S of a stage: the MFMAs of step S while decoding step S+1 of `cur`
+  // (step 0 of `nxt` when S == 7).  Steps 0-5 also issue two of the twelve
+  // global loads of stage kt+3 (slots 5 and 13); steps 2-5, after the barrier,
+  // read two of the next stage's fragments from LDS (slots 0 and 8).
   template <int S>
-  __device__ __forceinline__ void step_io(const Frags& cur, Frags& nxt, const uint8_t* nxt_st, lds_ptr_t load_buf,
-                                          int kt_load) {
+  __device__ __forceinline__ void step_s(const Frags& cur, Frags& nxt, const uint8_t* rd, lds_ptr_t ld, int kt_load) {
 #pragma unroll
     for (int q = 0; q < FM * FN; ++q) {
       mfma(S, q);
       if (q == 0) finish(S, 15);
-      if (q > 0) finish(S + 1, q - 1);
-      start(cur, S + 1, q);
-      if ((q & 7) == 0) read_frag(nxt, nxt_st, 2 * (S - 2) + (q >> 3));
-      if (S <= 3 && (q & 1) == 1 && 8 * (S - 2) + (q >> 1) < kLoadsPerStage) issue_one(load_buf, kt_load, 8 * (S - 2) + (q >> 1));
+      if (q > 0) finish((S + 1) & 7, q - 1);
+      if constexpr (S < 7) {
+        start(cur, S + 1, q);
+      } else {
+        start(nxt, 0, q);
+      }
+      if constexpr (S >= 2 && S <= 5) {
+        if ((q & 7) == 0) read_frag(nxt, rd, 2 * (S - 2) + (q >> 3));
+      }
+      if constexpr (S <= 5) {
+        if ((q & 7) == 5) issue_one(ld, kt_load, 2 * S + (q >> 3));
+      }
       fence();
     }
   }
 
   // One stage; `cur` holds stage kt (step 0 decoded but for chunk 15), stage
   // kt+1 sits in LDS buffer `rd` once every wave's loads of it have landed,
-  // and `ld` (the buffer of stage kt-1, already consumed into registers) takes
-  // the global loads of stage kt+3.  Loads and reads issued for stages past
-  // the end of K fetch data that is never multiplied.
+  // and `ld` (the buffer of stage kt-1, whose fragments every wave read during
+  // stage kt-2) takes the global loads of stage kt+3.  Loads and reads issued
+  // for stages past the end of K fetch data that is never multiplied.
   __device__ __forceinline__ void stage(int kt, const Frags& cur, Frags& nxt, const uint8_t* rd, lds_ptr_t ld) {
-    step<true, true>(0, cur, 1);
-    step<true, true>(1, cur, 2);
-    wait_vmcnt<kLoadsPerStage>();  // stage kt+1 landed; stage kt+2 may still be in flight
+    step_s<0>(cur, nxt, rd, ld, kt + 3);
+    step_s<1>(cur, nxt, rd, ld, kt + 3);
+    // stage kt+1 landed once at most stage kt+2's twelve loads and the four
+    // of stage kt+3 issued in steps 0-1 are outstanding
+    wait_vmcnt<kLoadsPerStage + 4>();
     lds_barrier();
-    step_io<2>(cur, nxt, rd, ld, kt + 3);
-    step_io<3>(cur, nxt, rd, ld, kt + 3);
-    step_io<4>(cur, nxt, rd, ld, kt + 3);
-    step_io<5>(cur, nxt, rd, ld, kt + 3);
-    step<true, true>(6, cur, 7);
-    step<true, true>(7, nxt, 0);
+    step_s<2>(cur, nxt, rd, ld, kt + 3);
+    step_s<3>(cur, nxt, rd, ld, kt + 3);
+    step_s<4>(cur, nxt, rd, ld, kt + 3);
+    step_s<5>(cur, nxt, rd, ld, kt + 3);
+    step_s<6>(cur, nxt, rd, ld, kt + 3);
+    step_s<7>(cur, nxt, rd, ld, kt + 3);
   }
 };
 
