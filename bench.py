@@ -32,15 +32,21 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A4 GEMM TFLOP/s incl. act-quant at 8K-token prefill; % of MFMA/HBM roofline"
 PEAK_F16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0
-GEMM_SRCS = [os.path.join(ROOT, "nvfp4_w4a4_block_quantize_amd", "csrc", f)
-             for f in ("gemm.hip", "gemm_fast.hip", "gemm_common.h", "nvfp4_device.h")]
+CSRC = os.path.join(ROOT, "nvfp4_w4a4_block_quantize_amd", "csrc")
+# sources of the GEMM kernel each workload's dominant launch runs (traffic counters
+# are tied to these; once they change, the stored counters no longer apply)
+KERNEL_SRCS = {
+    "gemm_fast": ("gemm_fast.hip", "gemm_common.h", "nvfp4_device.h"),
+    "gemm_decode": ("gemm_decode.hip", "nvfp4_device.h"),
+}
+WORKLOAD_KERNEL = {"gdn": "gemm_fast", "mlp": "gemm_fast", "long": "gemm_fast", "decode": "gemm_decode"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=None, help="timed steps (default 50; 1000 for decode)")
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="gdn", choices=["gdn", "mlp", "decode", "long"])
     p.add_argument("--seed", type=int, default=0)
@@ -51,9 +57,12 @@ def parse():
     return p.parse_args()
 
 
-def gemm_source_sha():
+def gemm_source_sha(workload):
     h = hashlib.sha256()
-    for p in GEMM_SRCS:
+    for name in KERNEL_SRCS[WORKLOAD_KERNEL[workload]]:
+        p = os.path.join(CSRC, name)
+        if not os.path.exists(p):
+            return None
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -68,7 +77,7 @@ def load_traffic(workload):
     except (OSError, ValueError):
         return None
     e = d.get(workload)
-    if not e or e.get("gemm_source_sha") != gemm_source_sha():
+    if not e or e.get("gemm_source_sha") != gemm_source_sha(workload):
         return None
     return e.get("hbm_bytes_per_launch")
 
@@ -142,7 +151,7 @@ def run(args):
             if ev is not None:
                 ev[j][2].record()
 
-    steps = args.steps if args.workload != "decode" else max(args.steps, 1000)
+    steps = args.steps if args.steps is not None else (1000 if args.workload == "decode" else 50)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -203,7 +212,8 @@ def run(args):
                       for lin, p, q, g in zip(lins, preps, q_ms, g_ms)],
             "a_dtype": lins[0].a_dtype, "c_dtype": "bf16", "act_gscale": "static (calibrated on a separate draw)",
             "weights": "pre-quantised per module, fuse-rescaled, not timed",
-            "weight_copies_rotated": rotate, "gemm_source_sha": gemm_source_sha(),
+            "weight_copies_rotated": rotate, "gemm_kernel": WORKLOAD_KERNEL[args.workload],
+            "gemm_source_sha": gemm_source_sha(args.workload),
         },
         "roofline": roof,
     }
