@@ -37,7 +37,7 @@ CSRC = os.path.join(ROOT, "nvfp4_w4a4_block_quantize_amd", "csrc")
 # are tied to these; once they change, the stored counters no longer apply)
 KERNEL_SRCS = {
     "gemm_fast": ("gemm_fast.hip", "gemm_common.h", "nvfp4_device.h"),
-    "gemm_decode": ("gemm_decode.hip", "nvfp4_device.h"),
+    "gemm_decode": ("gemm_decode.hip", "gemm_common.h", "nvfp4_device.h"),
 }
 WORKLOAD_KERNEL = {"gdn": "gemm_fast", "mlp": "gemm_fast", "long": "gemm_fast", "decode": "gemm_decode"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")

@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libnvfp4.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["nvfp4_abi.cpp", "quantize.hip", "fuse_rescale.hip", "gemm.hip", "gemm_fast.hip"]
+SOURCES = ["nvfp4_abi.cpp", "quantize.hip", "fuse_rescale.hip", "gemm.hip", "gemm_fast.hip", "gemm_decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

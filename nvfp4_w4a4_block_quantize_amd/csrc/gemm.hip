@@ -289,6 +289,9 @@ hipError_t launch_cfg(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, c
 hipError_t launch_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                        const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
                        const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream) {
+  if (gemm_decode_supported(m, n, k, a_codes, a_scales, w_codes, w_scales))
+    return launch_gemm_decode(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype, ldc,
+                              stream);
   if (gemm_fast_supported(m, n, k, a_codes, a_scales, w_codes, w_scales))
     return launch_gemm_fast(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype, ldc,
                             stream);

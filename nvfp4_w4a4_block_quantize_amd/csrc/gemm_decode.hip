@@ -1,0 +1,345 @@
+// Decode-shaped W4A4 GEMM for gfx950 (M <= 32): C = alpha * A_hat W_hat^T on
+// NVFP4 operands (news article "Qwen3.8-27B最激进4bit量化开源，权重显存暴降2.9倍！",
+// section 02: E2M1 codes, one E4M3 scale per 16 elements, one FP32 global
+// scale per tensor, both operands 4-bit).
+//
+// With a few activation rows the product is bound by streaming the weight
+// once from HBM (0.5625 B per weight element), not by MFMA.  What limits a
+// stream on CDNA is the number of cache-line requests a CU can keep in
+// flight, so every line a load instruction touches must be used whole:
+//
+//  * K is walked in super-groups of 256 elements: one 128-byte line of codes
+//    and 16 scale bytes per row.  The 16x16x32 MFMA layout puts a row on 4
+//    lanes (q = lane/16), so a lane owns 32 code bytes of the row (bytes
+//    32q..32q+31, elements 64q..64q+63, blocks 4q..4q+3): two 16-byte buffer
+//    loads issued back to back (offsets 32q and 32q+16) together read each
+//    row's line once, and one 4-byte load reads the lane's four scale bytes
+//    (the 4 lanes of a row read its 16 contiguous scale bytes).
+//  * MFMA step s (0..7) of a super-group takes code word s of every lane:
+//    lane q contributes elements 64q+8s..64q+8s+7 (block 4q + s/2) to the
+//    K = 32 of v_mfma_f32_16x16x32_f16.  A and W use the same map, so every
+//    k is summed exactly once.
+//  * A workgroup of 4 waves owns R = 16*T weight rows over the whole of K.
+//    Wave w takes super-groups w, w+4, w+8, ..., so the four waves read
+//    adjacent lines of the same rows at about the same time (DRAM page
+//    locality), and each wave multiplies every weight tile by the same
+//    decoded activation fragment (the activation decode is shared T ways and
+//    done once per workgroup).  The four partial sums are added in LDS at the
+//    end in a fixed order (deterministic).
+//  * The workgroup's scale rows (weight and activation, all of K) are staged
+//    in LDS at the start with coalesced 16-byte loads when they fit; 4-byte
+//    scale loads per row and super-group would cost as many cache-line
+//    requests as the code lines themselves.
+//  * Two super-groups of code loads per wave alternate in registers: the
+//    loads of super-group j+2 are issued as soon as j has been multiplied.
+//  * Decode as in the prefill kernel: v_cvt_scalef32_pk_f16_fp4 (scale 1.0)
+//    then one v_pk_mul_f16 by the E4M3 block scale converted to fp16 (both
+//    exact), products exact in fp32, FP32 accumulation in the MFMA.
+#include "gemm_common.h"
+#include "nvfp4_internal.h"
+
+namespace nvfp4 {
+namespace {
+
+using namespace gemm;
+
+constexpr int kWaves = 4;
+constexpr int kSuperK = 256;  // K elements per super-group: one 128-byte code line per row
+constexpr int kScaleLdsBytes = 32768;  // scale rows staged in LDS when they fit in this
+
+typedef float float4_v __attribute__((ext_vector_type(4)));
+
+#if defined(__HIP_DEVICE_COMPILE__)
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+__device__ __forceinline__ uint32_t word_at(const uint4 (&v)[2], int s) {
+  const uint4& h = v[s >> 2];
+  return (s & 3) == 0 ? h.x : (s & 3) == 1 ? h.y : (s & 3) == 2 ? h.z : h.w;
+}
+
+// one tile's share of a super-group: 32 code bytes and 4 scale bytes per lane
+struct Frag {
+  uint4 c[2];
+  uint32_t s;
+};
+
+template <int MT, int T>
+struct Super {
+  Frag w[T];
+  Frag a[MT];
+};
+
+#endif  // __HIP_DEVICE_COMPILE__
+
+// MT activation tiles of 16 rows (M <= 16*MT), T weight tiles of 16 rows per
+// workgroup, OCC waves per SIMD.  SL: the workgroup's scale rows (weight and
+// activation, all of K) are staged in LDS once, with coalesced 16-byte loads,
+// instead of 4 bytes per row and super-group from memory.
+template <int MT, int T, int OCC, bool SL, int OUT>
+__global__ __launch_bounds__(kThreads, OCC) void gemm_decode_kernel(int64_t M, int64_t N, int64_t K,
+                                                                  const uint8_t* __restrict__ a_codes,
+                                                                  const uint8_t* __restrict__ a_scales,
+                                                                  const float* __restrict__ a_gscale,
+                                                                  const uint8_t* __restrict__ w_codes,
+                                                                  const uint8_t* __restrict__ w_scales,
+                                                                  const float* __restrict__ w_gscale,
+                                                                  void* __restrict__ c, int64_t ldc) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int R = 16 * T;      // weight rows per workgroup
+  constexpr int kPitch = R + 4;  // fp32 words per staged partial row (pad breaks bank aliasing)
+  constexpr int kRows = 16 * MT; // activation rows per workgroup
+  constexpr int kPartBytes = kWaves * kRows * kPitch * 4;
+  constexpr int kLdsBytes = SL ? (kPartBytes > kScaleLdsBytes ? kPartBytes : kScaleLdsBytes) : kPartBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  float* const part = reinterpret_cast<float*>(lds);  // [kWaves][kRows * kPitch], after the main loop
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, q = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * R;
+
+  const int64_t code_ld = K / 2, scale_ld = K / 16;
+  const __amdgpu_buffer_rsrc_t wc_r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)w_codes, (short)0, (int)(N * code_ld), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ws_r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)w_scales, (short)0, (int)(N * scale_ld), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ac_r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a_codes, (short)0, (int)(M * code_ld), 0x00020000);
+  const __amdgpu_buffer_rsrc_t as_r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a_scales, (short)0, (int)(M * scale_ld), 0x00020000);
+
+  // per-lane row offsets; rows past the matrix repeat the last row (results never stored)
+  uint32_t wc_off[T], ws_off[T], ac_off[MT], as_off[MT];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    int64_t r = n0 + 16 * t + lr;
+    r = r < N ? r : N - 1;
+    wc_off[t] = (uint32_t)(r * code_ld + 32 * q);
+    ws_off[t] = (uint32_t)(r * scale_ld + 4 * q);
+  }
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    int64_t r = 16 * i + lr;
+    r = r < M ? r : M - 1;
+    ac_off[i] = (uint32_t)(r * code_ld + 32 * q);
+    as_off[i] = (uint32_t)(r * scale_ld + 4 * q);
+  }
+
+  // this wave's super-groups
+  const int G = (int)(K / kSuperK);
+  // super-groups wv, wv+4, wv+8, ...: the four waves read adjacent lines of
+  // the same rows at about the same time (DRAM page locality)
+  const int ng = (G - wv + kWaves - 1) / kWaves;
+  auto gidx = [&](int jj) { return wv + kWaves * jj; };
+
+  // scale rows in LDS: weight rows 0..R-1, then activation rows R..R+kRows-1
+  const int srow = (int)scale_ld;  // bytes per scale row
+  if constexpr (SL) {
+    const int chunks_per_row = srow / 16;
+    const int total = (R + kRows) * chunks_per_row;
+    for (int f = tid; f < total; f += kThreads) {
+      const int row = f / chunks_per_row, ch = f - row * chunks_per_row;
+      const uint8_t* src;
+      if (row < R) {
+        const int64_t r = min(n0 + row, N - 1);
+        src = w_scales + r * scale_ld;
+      } else {
+        const int64_t r = min((int64_t)(row - R), M - 1);
+        src = a_scales + r * scale_ld;
+      }
+      *reinterpret_cast<uint4*>(lds + row * srow + 16 * ch) = *reinterpret_cast<const uint4*>(src + 16 * ch);
+    }
+    __syncthreads();
+  }
+
+  auto load = [&](Super<MT, T>& b, int g) {
+    g = max(0, min(g, G - 1));
+    const int cs = g * (kSuperK / 2), ss = g * (kSuperK / 16);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      b.w[t].c[0] = load16(wc_r, wc_off[t], cs);
+      b.w[t].c[1] = load16(wc_r, wc_off[t], cs + 16);
+      if constexpr (!SL) b.w[t].s = load4(ws_r, ws_off[t], ss);
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      b.a[i].c[0] = load16(ac_r, ac_off[i], cs);
+      b.a[i].c[1] = load16(ac_r, ac_off[i], cs + 16);
+      if constexpr (!SL) b.a[i].s = load4(as_r, as_off[i], ss);
+    }
+    // each super-group's loads stay together and in issue order (prologue and
+    // loop alike), so the wait before its use counts only the one issued after it
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  float4_v acc[MT][T];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[i][t] = float4_v{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](Super<MT, T>& b, int g) {
+    if constexpr (SL) {
+      // this lane's four scale bytes of super-group g (blocks 4q..4q+3)
+      const int off = g * 16 + 4 * q;
+#pragma unroll
+      for (int t = 0; t < T; ++t) b.w[t].s = *reinterpret_cast<const uint32_t*>(lds + (16 * t + lr) * srow + off);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        b.a[i].s = *reinterpret_cast<const uint32_t*>(lds + (R + 16 * i + lr) * srow + off);
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      // scale byte s/2 of a lane's four, as an fp16 pair (exact), broadcast
+      auto scale_of = [&](uint32_t w) {
+        const half2_t sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w >> (16 * (s >> 2)), 1.0f, false);
+        const _Float16 v = sp[(s >> 1) & 1];
+        return half2_t{v, v};
+      };
+      half8_t fa[MT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) fa[i] = decode8(word_at(b.a[i].c, s), scale_of(b.a[i].s));
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const half8_t fw = decode8(word_at(b.w[t].c, s), scale_of(b.w[t].s));
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw, fa[i], acc[i][t], 0, 0, 0);
+        // one weight fragment per scheduling region: decoding a whole step (or
+        // several) up front would run out of registers at three waves per SIMD
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // two super-groups in flight; loads past this wave's range re-read its last
+  // super-group (cache hits, never multiplied)
+  Super<MT, T> b0, b1;
+  load(b0, gidx(0));
+  load(b1, gidx(min(1, max(ng - 1, 0))));
+  int j = 0;
+  for (; j + 2 <= ng; j += 2) {
+    compute(b0, gidx(j));
+    load(b0, gidx(min(j + 2, ng - 1)));
+    compute(b1, gidx(j + 1));
+    load(b1, gidx(min(j + 3, ng - 1)));
+  }
+  if (j < ng) compute(b0, gidx(j));
+  if constexpr (SL) __syncthreads();  // the partial sums reuse the scale rows' LDS
+
+  // acc[i][t]: lane holds activation row 16i + lane%16 and weight rows
+  // 16t + 4q + 0..3
+  float* mine = part + wv * (kRows * kPitch);
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      *reinterpret_cast<float4_v*>(mine + (16 * i + lr) * kPitch + 16 * t + 4 * q) = acc[i][t];
+  __syncthreads();
+
+  // sum the four waves' partial sums in a fixed order, apply alpha, store 4 columns per thread
+  const float alpha = 1.0f / (*a_gscale * *w_gscale);
+  constexpr int kRuns = R / 4;  // runs of 4 columns per row
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(c) % 16) == 0 && (ldc * (OUT == 0 ? 4 : 2)) % 16 == 0;
+  for (int f = tid; f < kRows * kRuns; f += kThreads) {
+    const int row = f / kRuns, run = f % kRuns;
+    const int64_t m = row;
+    const int64_t n = n0 + 4 * run;
+    if (m >= M || n >= N) continue;
+    float4_v s = *reinterpret_cast<const float4_v*>(part + row * kPitch + 4 * run);
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+      s += *reinterpret_cast<const float4_v*>(part + w * (kRows * kPitch) + row * kPitch + 4 * run);
+    const float o[4] = {s[0] * alpha, s[1] * alpha, s[2] * alpha, s[3] * alpha};
+    if constexpr (OUT == 0) {
+      float* p = static_cast<float*>(c) + m * ldc + n;
+      if (n + 3 < N && vec_ok) {
+        *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < N) p[e] = o[e];
+      }
+    } else {
+      uint16_t* p = static_cast<uint16_t*>(c) + m * ldc + n;
+      uint16_t b[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (OUT == 1) {
+          b[e] = (uint16_t)bf16_rne_bits(o[e]);
+        } else {
+          const _Float16 hv = (_Float16)o[e];
+          __builtin_memcpy(&b[e], &hv, 2);
+        }
+      }
+      if (n + 3 < N && (reinterpret_cast<uintptr_t>(p) % 8) == 0) {
+        *reinterpret_cast<uint2*>(p) = make_uint2((uint32_t)b[0] | ((uint32_t)b[1] << 16),
+                                                  (uint32_t)b[2] | ((uint32_t)b[3] << 16));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < N) p[e] = b[e];
+      }
+    }
+  }
+#endif
+}
+
+template <int MT, int T, int OCC>
+hipError_t launch_decode_cfg(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
+                             const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
+                             const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream) {
+  const unsigned grid = (unsigned)((n + 16 * T - 1) / (16 * T));
+  // staged scale rows: all of them must fit, and 16-byte loads need 16-byte aligned rows
+  const bool sl = (int64_t)(16 * T + 16 * MT) * (k / 16) <= kScaleLdsBytes &&
+                  (reinterpret_cast<uintptr_t>(a_scales) % 16) == 0 && (reinterpret_cast<uintptr_t>(w_scales) % 16) == 0;
+#define NVFP4_LAUNCH(SLV, OUT)                                                                                     \
+  gemm_decode_kernel<MT, T, OCC, SLV, OUT><<<grid, kThreads, 0, stream>>>(m, n, k, a_codes, a_scales, a_gscale, \
+                                                                         w_codes, w_scales, w_gscale, c, ldc)
+#define NVFP4_LAUNCH_OUT(SLV)   \
+  if (out_dtype == 0)           \
+    NVFP4_LAUNCH(SLV, 0);       \
+  else if (out_dtype == 1)      \
+    NVFP4_LAUNCH(SLV, 1);       \
+  else                          \
+    NVFP4_LAUNCH(SLV, 2);
+  if (sl) {
+    NVFP4_LAUNCH_OUT(true)
+  } else {
+    NVFP4_LAUNCH_OUT(false)
+  }
+#undef NVFP4_LAUNCH_OUT
+#undef NVFP4_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_decode_supported(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
+                           const uint8_t* w_codes, const uint8_t* w_scales) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(a_codes) % 16) == 0 &&
+                       (reinterpret_cast<uintptr_t>(w_codes) % 16) == 0 &&
+                       (reinterpret_cast<uintptr_t>(a_scales) % 4) == 0 &&
+                       (reinterpret_cast<uintptr_t>(w_scales) % 4) == 0;
+  // buffer offsets and sizes are 32-bit
+  const bool fits = n * (k / 2) < ((int64_t)1 << 31) && m * (k / 2) < ((int64_t)1 << 31);
+  return aligned && fits && m <= 32 && k % kSuperK == 0;
+}
+
+hipError_t launch_gemm_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
+                              const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
+                              const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream) {
+  if (m <= 16)
+    return launch_decode_cfg<1, 4, 3>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype,
+                                      ldc, stream);
+  return launch_decode_cfg<2, 3, 3>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype,
+                                    ldc, stream);
+}
+
+}  // namespace nvfp4
