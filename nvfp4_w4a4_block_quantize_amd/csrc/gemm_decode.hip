@@ -141,23 +141,13 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_decode_kernel(int64_t M, i
 
   // scale rows in LDS: weight rows 0..R-1, then activation rows R..R+kRows-1
   const int srow = (int)scale_ld;  // bytes per scale row
-  if constexpr (SL) {
-    const int chunks_per_row = srow / 16;
-    const int total = (R + kRows) * chunks_per_row;
-    for (int f = tid; f < total; f += kThreads) {
-      const int row = f / chunks_per_row, ch = f - row * chunks_per_row;
-      const uint8_t* src;
-      if (row < R) {
-        const int64_t r = min(n0 + row, N - 1);
-        src = w_scales + r * scale_ld;
-      } else {
-        const int64_t r = min((int64_t)(row - R), M - 1);
-        src = a_scales + r * scale_ld;
-      }
-      *reinterpret_cast<uint4*>(lds + row * srow + 16 * ch) = *reinterpret_cast<const uint4*>(src + 16 * ch);
-    }
-    __syncthreads();
-  }
+  const int chunks_per_row = srow / 16;
+  const int n_chunks = (R + kRows) * chunks_per_row;
+  // row = chunk / chunks_per_row by a multiply with ceil(2^32 / chunks_per_row)
+  // and a shift: exact for chunk < 2^14 and chunks_per_row < 2^12
+  const uint64_t row_mag = (0xFFFFFFFFull + (uint64_t)chunks_per_row) / (uint64_t)chunks_per_row;
+  auto chunk_row = [&](int f) { return (int)(((uint64_t)(uint32_t)f * row_mag) >> 32); };
+  constexpr int kChunksPer = kScaleLdsBytes / 16 / kThreads;  // the host guarantees n_chunks fits
 
   auto load = [&](Super<MT, T>& b, int g) {
     g = max(0, min(g, G - 1));
@@ -220,9 +210,36 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_decode_kernel(int64_t M, i
 
   // two super-groups in flight; loads past this wave's range re-read its last
   // super-group (cache hits, never multiplied)
+  // the first two super-groups' code loads go out first, the scale-row
+  // staging loads right behind them, so both latencies overlap
   Super<MT, T> b0, b1;
   load(b0, gidx(0));
   load(b1, gidx(min(1, max(ng - 1, 0))));
+  if constexpr (SL) {
+    // straight-line, clamped (always valid) chunk indices: every load is
+    // issued before the first wait; a thread past the end repeats the last
+    // chunk and writes the same bytes to the same place
+    uint4 stage[kChunksPer];
+#pragma unroll
+    for (int u = 0; u < kChunksPer; ++u) {
+      const int f = min(tid + u * kThreads, n_chunks - 1);
+      const int row = chunk_row(f), ch = f - row * chunks_per_row;
+      // both candidate rows computed, then selected (no branch around the load)
+      const bool wrow = row < R;
+      const int rw = (int)min(n0 + row, N - 1), ra = (int)min((int64_t)(row - R), M - 1);
+      const uint8_t* base = wrow ? w_scales : a_scales;
+      const int r = wrow ? rw : ra;
+      stage[u] = *reinterpret_cast<const uint4*>(base + (int64_t)r * scale_ld + 16 * ch);
+    }
+#pragma unroll
+    for (int u = 0; u < kChunksPer; ++u) {
+      const int f = min(tid + u * kThreads, n_chunks - 1);
+      const int row = chunk_row(f), ch = f - row * chunks_per_row;
+      *reinterpret_cast<uint4*>(lds + row * srow + 16 * ch) = stage[u];
+    }
+    __syncthreads();
+  }
+
   int j = 0;
   for (; j + 2 <= ng; j += 2) {
     compute(b0, gidx(j));
