@@ -17,6 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libnvfp4.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+CONFORMANCE_PATH = os.path.join(HERE, "conformance_cvt")
 
 SOURCES = ["nvfp4_abi.cpp", "quantize.hip", "fuse_rescale.hip", "gemm.hip", "gemm_fast.hip", "gemm_decode.hip"]
 
@@ -57,8 +58,15 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
+    # conformance check of the conversion instructions the kernels rely on
+    # (a standalone program, run by the GPU tests)
+    cmd = [HIPCC, *COMMON_FLAGS, os.path.join(CSRC, "conformance_cvt.hip"), "-o", CONFORMANCE_PATH + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for conformance_cvt.hip:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(CONFORMANCE_PATH + ".tmp", CONFORMANCE_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {CONFORMANCE_PATH}")
     return LIB_PATH
 
 

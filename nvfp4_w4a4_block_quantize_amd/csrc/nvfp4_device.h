@@ -35,14 +35,4 @@ __device__ __forceinline__ float f32_from_e4m3(uint32_t byte) {
   return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
 }
 
-// E2M1 code of an fp32 value: nearest grid value, ties to the even code,
-// |y| > 6 saturates to 6; the sign bit is copied from y (so -0.0 gives 0x8).
-__device__ __forceinline__ uint32_t e2m1_from_f32(float y) {
-  const float a = __builtin_fabsf(y);
-  const uint32_t mag = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                       (uint32_t)(a > 5.0f);
-  return mag | ((__float_as_uint(y) >> 28) & 8u);
-}
-
 }  // namespace nvfp4

@@ -15,7 +15,10 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;  // independent 8-element chunks per thread, loads issued together
+// independent 8-element chunks per thread, loads issued together; small
+// tensors use one per thread so that more workgroups share the latency
+constexpr int kUnrollLarge = 4;
+constexpr int64_t kSmallChunks = (int64_t)1 << 18;
 
 struct Raw {
   u32x4_t a;
@@ -69,19 +72,26 @@ __device__ __forceinline__ void widen(const Raw& r, float (&f)[8]) {
 }
 
 // Quantise one lane's 8 elements given the block max shared with its partner.
+// The E2M1 rounding of y = fp32(x * r) is v_cvt_scalef32_pk_fp4_f32 with a
+// scale of 1.0: nearest value, ties to the even code, saturation at 6, sign
+// bit from y (so -0.0 gives 0x8).  That equals the element rule for every
+// non-NaN fp32 input (checked exhaustively over all 2^32 bit patterns on
+// gfx950), and each instruction writes two codes into one byte of the word,
+// even element in the low nibble.
 __device__ __forceinline__ uint32_t encode8(const float (&f)[8], float g, float amax_b, uint32_t* scale_out) {
   // s = fp32(fp32(amax_b / 6) * g); IEEE division (correctly rounded), no contraction
   const float s = (amax_b / 6.0f) * g;
   const uint32_t S = e4m3_from_f32(s);
   const float r = (S == 0u) ? 0.0f : g / f32_from_e4m3(S);
-  uint32_t word = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) word |= e2m1_from_f32(f[i] * r) << (4 * i);
+  uint32_t word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, f[0] * r, f[1] * r, 1.0f, 0);
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, f[2] * r, f[3] * r, 1.0f, 1);
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, f[4] * r, f[5] * r, 1.0f, 2);
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, f[6] * r, f[7] * r, 1.0f, 3);
   *scale_out = S;
   return word;
 }
 
-template <int DT, bool DENSE>
+template <int DT, bool DENSE, int kUnroll>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const void* __restrict__ x, int64_t total_chunks,
                                                             uint32_t chunks_per_row, int64_t ldx,
                                                             const float* __restrict__ gscale,
@@ -175,10 +185,16 @@ hipError_t launch_typed(const void* x, int64_t rows, int64_t cols, int64_t ldx, 
                                                                      reinterpret_cast<uint32_t*>(gscale));
     finalize_gscale_kernel<<<1, 1, 0, stream>>>(gscale);
   }
-  const int64_t per_block = (int64_t)kThreads * kUnroll;
-  const int64_t blocks = (total + per_block - 1) / per_block;
-  quantize_kernel<DT, DENSE><<<(unsigned)blocks, kThreads, 0, stream>>>(
-      x, total, (uint32_t)chunks_per_row, ldx, gscale, reinterpret_cast<uint32_t*>(codes), scales);
+  if (total < kSmallChunks) {
+    const int64_t blocks = (total + kThreads - 1) / kThreads;
+    quantize_kernel<DT, DENSE, 1><<<(unsigned)blocks, kThreads, 0, stream>>>(
+        x, total, (uint32_t)chunks_per_row, ldx, gscale, reinterpret_cast<uint32_t*>(codes), scales);
+  } else {
+    const int64_t per_block = (int64_t)kThreads * kUnrollLarge;
+    const int64_t blocks = (total + per_block - 1) / per_block;
+    quantize_kernel<DT, DENSE, kUnrollLarge><<<(unsigned)blocks, kThreads, 0, stream>>>(
+        x, total, (uint32_t)chunks_per_row, ldx, gscale, reinterpret_cast<uint32_t*>(codes), scales);
+  }
   return hipGetLastError();
 }
 

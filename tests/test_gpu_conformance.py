@@ -1,0 +1,23 @@
+"""The gfx950 conversion instructions the kernels rely on, checked against the
+rules they implement: the quantiser's E2M1 encoding for every non-NaN fp32
+input, and the GEMM's E2M1 / E4M3 decodes for every code (see
+nvfp4_w4a4_block_quantize_amd/csrc/conformance_cvt.hip)."""
+import os
+import subprocess
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+EXE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "nvfp4_w4a4_block_quantize_amd",
+                   "conformance_cvt")
+
+
+def test_conversion_instructions_match_the_format_rules(gpu_lib):
+    if not os.path.exists(EXE):
+        pytest.fail(f"{EXE} is missing: run the build first")
+    print("[case] conformance_cvt", flush=True)
+    res = subprocess.run([EXE], capture_output=True, text=True, timeout=100)
+    print(res.stdout, flush=True)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert res.stdout.count(": 0 mismatches") == 2, res.stdout
