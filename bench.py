@@ -38,8 +38,10 @@ CSRC = os.path.join(ROOT, "nvfp4_w4a4_block_quantize_amd", "csrc")
 KERNEL_SRCS = {
     "gemm_fast": ("gemm_fast.hip", "gemm_common.h", "nvfp4_device.h"),
     "gemm_decode": ("gemm_decode.hip", "gemm_common.h", "nvfp4_device.h"),
+    "amax_observe": ("quantize.hip", "nvfp4_device.h"),
 }
-WORKLOAD_KERNEL = {"gdn": "gemm_fast", "mlp": "gemm_fast", "long": "gemm_fast", "decode": "gemm_decode"}
+WORKLOAD_KERNEL = {"gdn": "gemm_fast", "mlp": "gemm_fast", "long": "gemm_fast", "decode": "gemm_decode",
+                   "calib": "amax_observe"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
@@ -48,7 +50,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None, help="timed steps (default 50; 1000 for decode)")
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="gdn", choices=["gdn", "mlp", "decode", "long"])
+    p.add_argument("--workload", default="gdn", choices=["gdn", "mlp", "decode", "long", "calib"],
+                   help="calib: the calibration observer over 32K-token batches (HBM-bound, GB/s)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=8192, help="activation rows in the oracle's timed sample")
@@ -124,6 +127,63 @@ class Prepared:
 
     def quant_bytes(self):
         return self.m * self.k * self.a.element_size() + self.m * (self.k // 2 + self.k // 16)
+
+
+def copy_calibration(torch):
+    """A plain 1 GiB device-to-device copy: the known size that HBM byte
+    counters are scaled against."""
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    return nbytes
+
+
+def run_calib(args):
+    """Calibration observer: max|x| of one 32K-token batch of hidden size 5120
+    (bf16, 335.5 MB) folded into a device word per step; bytes = the batch."""
+    import torch
+
+    import nvfp4_w4a4_block_quantize_amd as nv
+    from nvfp4_w4a4_block_quantize_amd import synth
+
+    nv.load_library()
+    rows, cols = 32768, synth.HIDDEN
+    batches = []
+    for i in range(2):  # two resident batches, alternated, 671 MB > the 256 MB Infinity Cache
+        x, _ = synth.activations(args.seed, "long", 500 + i, rows, cols, dist="t3")
+        batches.append(torch.from_numpy(x).cuda().to(torch.bfloat16))
+        del x
+    state = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    steps = args.steps if args.steps is not None else 50
+    for i in range(args.warmup):
+        nv.nvfp4_amax_observe(batches[i % 2], state)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        nv.nvfp4_amax_observe(batches[i % 2], state)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    byts = rows * cols * 2
+    gbs = byts / (ms * 1e-3) / 1e9
+    g = nv.nvfp4_gscale_from_amax(state)
+    out = {"metric": "calibration observer GB/s (max|x| over 32K-token batches), % of HBM roofline",
+           "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16 in, f32 max", "data": "synthetic (seeded; no dataset)",
+           "config": {"workload": "calib_observer_32k_x_5120", "batch": [rows, cols], "gscale": float(g.item()),
+                      "kernel_source_sha": gemm_source_sha("calib")},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": load_traffic("calib"),
+                        "kernel": "amax_kernel (observer)", "avg_ms": round(ms, 5)}}
+    if args.copy_calibration:
+        out["copy_calibration_bytes"] = copy_calibration(torch)
+    print(json.dumps(out), flush=True)
 
 
 def run(args):
@@ -218,13 +278,7 @@ def run(args):
         "roofline": roof,
     }
     if args.copy_calibration:
-        nbytes = 1 << 30
-        src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        out["copy_calibration_bytes"] = nbytes
+        out["copy_calibration_bytes"] = copy_calibration(torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(lins, args.cpu_rows, args.workload)
     print(json.dumps(out), flush=True)
@@ -276,7 +330,10 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus_requested": args.gpus}), flush=True)
         sys.exit(2)
-    run(args)
+    if args.workload == "calib":
+        run_calib(args)
+    else:
+        run(args)
 
 
 if __name__ == "__main__":

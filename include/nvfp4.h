@@ -95,6 +95,33 @@ nvfp4_status nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_
                             void* stream);
 
 /*
+ * nvfp4_amax_observe / nvfp4_gscale_from_amax — static activation global
+ * scale from calibration data (the paper reading, section 四 4.1, and the news
+ * article, section 03: the checkpoint is calibrated on 128 samples of 32K
+ * tokens; the activation global scale then serves every later input).
+ *
+ * nvfp4_amax_observe folds max|x| of one batch into *amax_state:
+ *   x           [rows][ldx] elements of type x_dtype (NVFP4_F32 / BF16 / F16),
+ *               16-byte aligned, ldx * sizeof(element) a multiple of 16,
+ *               cols a multiple of 8.
+ *   amax_state  device fp32[1], owned by the caller, set to 0.0f (all bytes
+ *               zero) before the first batch.  After any number of calls on
+ *               the stream it holds the largest magnitude seen; max is exact
+ *               and independent of order, so the result does not depend on
+ *               batch order or launch configuration.  Calls may be
+ *               concurrent on different streams.
+ * nvfp4_gscale_from_amax writes *gscale = fp32(2688 / amax) (1.0 when amax is
+ * 0): the encode global scale of the whole calibration set, ready for
+ * nvfp4_quantize's static mode.  Both pointers are device fp32[1].
+ *
+ * Errors: NULL pointers -> ERR_NULL; rows <= 0, cols <= 0, cols % 8 != 0,
+ * ldx < cols -> ERR_SHAPE; alignment -> ERR_ALIGN; bad x_dtype -> ERR_DTYPE.
+ */
+nvfp4_status nvfp4_amax_observe(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                float* amax_state, void* stream);
+nvfp4_status nvfp4_gscale_from_amax(const float* amax_state, float* gscale, void* stream);
+
+/*
  * nvfp4_fuse_rescale — checkpoint-side repair of a fused group of separately
  * calibrated modules (news article section 03: bring every tensor of the group
  * to one global scale and fold the ratio into its E4M3 block scales; the

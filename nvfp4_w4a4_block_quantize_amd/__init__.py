@@ -6,6 +6,8 @@ current stream; there is no fallback path: if the library is missing or no
 GPU is visible, the calls raise.
 
 Functions carry the C names:
+  nvfp4_amax_observe(x, amax_state)          -> amax_state
+  nvfp4_gscale_from_amax(amax_state)         -> gscale
   nvfp4_quantize(x, gscale, mode)            -> (codes, scales)
   nvfp4_fuse_rescale(scales, k, rows, gs)    -> (g_star, lossy_blocks)
   nvfp4_gemm(a_codes, a_scales, a_gscale,
@@ -35,6 +37,8 @@ SIGNATURES = {
     "nvfp4_quantize": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _I32, _P, _P, _P]),
     "nvfp4_fuse_rescale": (_I32, [_P, _I64, _I32, _P, _P, _P, _P, _P]),
     "nvfp4_gemm": (_I32, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _P]),
+    "nvfp4_amax_observe": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P]),
+    "nvfp4_gscale_from_amax": (_I32, [_P, _P, _P]),
     "nvfp4_status_str": (ctypes.c_char_p, [_I32]),
     "nvfp4_abi_version": (_I32, []),
 }
@@ -122,6 +126,29 @@ def nvfp4_quantize(x, gscale, mode: str = "static", codes=None, scales=None, str
                                        _stream_ptr(stream))
     _check("nvfp4_quantize", st)
     return codes, scales
+
+
+def nvfp4_amax_observe(x, amax_state, stream=None):
+    """Fold max|x| of one calibration batch (2-D GPU tensor) into amax_state,
+    a GPU float32 tensor with one element that starts at 0."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    st = load_library().nvfp4_amax_observe(_dev(x, "x"), _dtype_code(x.dtype), rows, cols, x.stride(0),
+                                           _dev(amax_state, "amax_state"), _stream_ptr(stream))
+    _check("nvfp4_amax_observe", st)
+    return amax_state
+
+
+def nvfp4_gscale_from_amax(amax_state, gscale=None, stream=None):
+    """Encode global scale fp32(2688 / amax) of the observed calibration set."""
+    torch = _torch()
+    if gscale is None:
+        gscale = torch.empty(1, dtype=torch.float32, device=amax_state.device)
+    st = load_library().nvfp4_gscale_from_amax(_dev(amax_state, "amax_state"), _dev(gscale, "gscale"),
+                                               _stream_ptr(stream))
+    _check("nvfp4_gscale_from_amax", st)
+    return gscale
 
 
 def nvfp4_fuse_rescale(scales, k: int, module_rows, module_gscales, want_lossy: bool = True, stream=None):

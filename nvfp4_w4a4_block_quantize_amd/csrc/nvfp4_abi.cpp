@@ -78,6 +78,29 @@ nvfp4_status nvfp4_quantize(const void* x, int32_t x_dtype, int64_t rows, int64_
   return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_DEVICE;
 }
 
+nvfp4_status nvfp4_amax_observe(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                float* amax_state, void* stream) {
+  if (!x || !amax_state) return NVFP4_ERR_NULL;
+  const int es = dtype_size(x_dtype);
+  if (es == 0) return NVFP4_ERR_DTYPE;
+  if (rows <= 0 || cols <= 0 || cols % 8 != 0 || ldx < cols || rows >= kMaxDim || cols >= kMaxDim ||
+      ldx >= ((int64_t)1 << 40))
+    return NVFP4_ERR_SHAPE;
+  if (!aligned(x, 16) || (ldx * es) % 16 != 0 || !aligned(amax_state, 4)) return NVFP4_ERR_ALIGN;
+  if (!device_ok()) return NVFP4_ERR_DEVICE;
+  const hipError_t e =
+      nvfp4::launch_amax_observe(x, x_dtype, rows, cols, ldx, amax_state, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_DEVICE;
+}
+
+nvfp4_status nvfp4_gscale_from_amax(const float* amax_state, float* gscale, void* stream) {
+  if (!amax_state || !gscale) return NVFP4_ERR_NULL;
+  if (!aligned(amax_state, 4) || !aligned(gscale, 4)) return NVFP4_ERR_ALIGN;
+  if (!device_ok()) return NVFP4_ERR_DEVICE;
+  const hipError_t e = nvfp4::launch_gscale_from_amax(amax_state, gscale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_DEVICE;
+}
+
 nvfp4_status nvfp4_fuse_rescale(uint8_t* scales, int64_t k, int32_t n_modules, const int64_t* module_rows,
                                 const float* module_gscales, float* shared_gscale, int64_t* lossy_blocks,
                                 void* stream) {

@@ -12,6 +12,12 @@ namespace nvfp4 {
 hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, float* gscale,
                            bool dynamic, uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
+// Calibration observer: atomically folds max|x| into the fp32 word *amax_state
+// (non-negative floats order like their bit patterns); then g = 2688 / amax.
+hipError_t launch_amax_observe(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, float* amax_state,
+                               hipStream_t stream);
+hipError_t launch_gscale_from_amax(const float* amax_state, float* gscale, hipStream_t stream);
+
 // Fold rho = g_star / g_module into `count` scale bytes starting at `scales`;
 // adds the number of changed dequantisation factors to *lossy when non-null.
 hipError_t launch_fuse_rescale(uint8_t* scales, int64_t count, float g_star, float g_module, int64_t* lossy,

@@ -145,25 +145,52 @@ template <int DT, bool DENSE>
 __global__ __launch_bounds__(kThreads) void amax_kernel(const void* __restrict__ x, int64_t total_chunks,
                                                         uint32_t chunks_per_row, int64_t ldx,
                                                         uint32_t* __restrict__ amax_bits) {
+  // four chunks per thread and iteration, loads issued together
+  constexpr int kU = 4;
   float m = 0.0f;
-  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < total_chunks;
-       c += (int64_t)gridDim.x * kThreads) {
-    int64_t elem;
-    if constexpr (DENSE) {
-      elem = c * 8;
-    } else {
-      const int64_t row = c / chunks_per_row;
-      elem = row * ldx + (c - row * chunks_per_row) * 8;
-    }
-    float f[8];
-    widen<DT>(load_chunk<DT>(x, elem), f);
+  const int64_t step = (int64_t)gridDim.x * kThreads * kU;
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads * kU + threadIdx.x; c0 < total_chunks; c0 += step) {
+    Raw raw[kU];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
+    for (int u = 0; u < kU; ++u) {
+      const int64_t c = c0 + (int64_t)u * kThreads;
+      if (c < total_chunks) {
+        int64_t elem;
+        if constexpr (DENSE) {
+          elem = c * 8;
+        } else {
+          const int64_t row = c / chunks_per_row;
+          elem = row * ldx + (c - row * chunks_per_row) * 8;
+        }
+        raw[u] = load_chunk<DT>(x, elem);
+      } else {
+        raw[u].a = u32x4_t{0, 0, 0, 0};
+        raw[u].b = u32x4_t{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      float f[8];
+      widen<DT>(raw[u], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(f[i]));
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
-  // non-negative floats order like their bit patterns, so an integer max is exact
-  if ((threadIdx.x & 63) == 0) atomicMax(amax_bits, __float_as_uint(m));
+  // one value per workgroup, and an atomic only when it would raise the word:
+  // thousands of atomics on one address serialise in the L2.  Non-negative
+  // floats order like their bit patterns, so an integer max is exact.
+  __shared__ float wave_max[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = wave_max[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) b = __builtin_fmaxf(b, wave_max[w]);
+    const uint32_t bits = __float_as_uint(b);
+    if (bits > __hip_atomic_load(amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(amax_bits, bits);
+  }
 }
 
 __global__ void finalize_gscale_kernel(float* gscale) {
@@ -198,7 +225,46 @@ hipError_t launch_typed(const void* x, int64_t rows, int64_t cols, int64_t ldx, 
   return hipGetLastError();
 }
 
+__global__ void gscale_from_amax_kernel(const float* amax_state, float* gscale) {
+  const float amax = *amax_state;
+  *gscale = amax > 0.0f ? kGlobalScaleNumerator / amax : 1.0f;
+}
+
+template <int DT, bool DENSE>
+hipError_t launch_observe_typed(const void* x, int64_t rows, int64_t cols, int64_t ldx, float* amax_state,
+                                hipStream_t stream) {
+  const int64_t chunks_per_row = cols / 8;
+  const int64_t total = rows * chunks_per_row;
+  int64_t blocks = (total + kThreads - 1) / kThreads;
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  if (blocks > cap) blocks = cap;
+  amax_kernel<DT, DENSE><<<(unsigned)blocks, kThreads, 0, stream>>>(x, total, (uint32_t)chunks_per_row, ldx,
+                                                                   reinterpret_cast<uint32_t*>(amax_state));
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_amax_observe(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, float* amax_state,
+                               hipStream_t stream) {
+  const bool dense = (ldx == cols);
+  switch (dtype) {
+    case 0:
+      return dense ? launch_observe_typed<0, true>(x, rows, cols, ldx, amax_state, stream)
+                   : launch_observe_typed<0, false>(x, rows, cols, ldx, amax_state, stream);
+    case 1:
+      return dense ? launch_observe_typed<1, true>(x, rows, cols, ldx, amax_state, stream)
+                   : launch_observe_typed<1, false>(x, rows, cols, ldx, amax_state, stream);
+    default:
+      return dense ? launch_observe_typed<2, true>(x, rows, cols, ldx, amax_state, stream)
+                   : launch_observe_typed<2, false>(x, rows, cols, ldx, amax_state, stream);
+  }
+}
+
+hipError_t launch_gscale_from_amax(const float* amax_state, float* gscale, hipStream_t stream) {
+  gscale_from_amax_kernel<<<1, 1, 0, stream>>>(amax_state, gscale);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx, float* gscale,
                            bool dynamic, uint8_t* codes, uint8_t* scales, hipStream_t stream) {

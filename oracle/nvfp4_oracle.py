@@ -176,6 +176,24 @@ def global_scale(x):
     return np.float32(GLOBAL_SCALE_NUMERATOR / amax)
 
 
+def calibrate_ref(batches):
+    """Static activation global scale from a calibration set: the encode scale
+    of everything the observer saw, g = fp32(2688 / max_i max|batch_i|), 1.0
+    when every value is zero (the paper reading, section 四 4.1, and the news
+    article, section 03: activations are calibrated once, on 128 samples of
+    32K tokens).  The largest magnitude is folded batch by batch, as the
+    observer does; max is exact, so the fold equals the maximum over the
+    concatenation."""
+    amax = np.float32(0.0)
+    for b in batches:
+        b = np.asarray(b, dtype=np.float32)
+        if b.size:
+            amax = max(amax, np.float32(np.max(np.abs(b))))
+    if amax == 0:
+        return amax, np.float32(1.0)
+    return amax, np.float32(GLOBAL_SCALE_NUMERATOR / amax)
+
+
 def quantize_ref(x, g=None):
     """NVFP4 quantisation of a [rows, cols] array (cols % 16 == 0).
 

@@ -109,3 +109,18 @@ def test_fuse_rescale_validation_writes_nothing_on_error(lib):
     assert f(lib, gs=(float("nan"), 1.0)) == (5, -1.0)
     assert f(lib, rows=(), gs=()) == (5, -1.0)
     assert f(lib, rows=(1,) * 65, gs=(1.0,) * 65) == (5, -1.0)
+
+
+def test_amax_observe_validation(lib):
+    obs = lib.nvfp4_amax_observe
+    assert obs(None, 1, 4, 32, 32, P, None) == 1
+    assert obs(P, 1, 4, 32, 32, None, None) == 1
+    assert obs(P, 7, 4, 32, 32, P, None) == 4
+    assert obs(P, 1, 0, 32, 32, P, None) == 2
+    assert obs(P, 1, 4, 12, 12, P, None) == 2   # cols not a multiple of 8
+    assert obs(P, 1, 4, 32, 16, P, None) == 2   # ldx < cols
+    assert obs(P + 8, 1, 4, 32, 32, P, None) == 3
+    assert obs(P, 1, 4, 32, 36, P, None) == 3   # row pitch not a multiple of 16 bytes
+    assert lib.nvfp4_gscale_from_amax(None, P, None) == 1
+    assert lib.nvfp4_gscale_from_amax(P, None, None) == 1
+    assert lib.nvfp4_gscale_from_amax(P + 2, P, None) == 3

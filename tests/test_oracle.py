@@ -270,3 +270,26 @@ def test_fuse_rejects_bad_global_scales():
         O.fuse_rescale_ref(np.zeros((2, 1), np.uint8), [1, 1], [1.0, 0.0])
     with pytest.raises(ValueError):
         O.fuse_rescale_ref(np.zeros((2, 1), np.uint8), [1, 1], [1.0, float("nan")])
+
+
+# ---- calibration observer (static activation global scale)
+
+def test_calibration_hand_example():
+    # largest magnitude 7 over three batches: g = 2688 / 7 = 384 exactly
+    amax, g = O.calibrate_ref([np.array([[1.0, -3.0]]), np.array([[2.5, 0.5]]), np.array([[-7.0, 0.0]])])
+    assert amax == np.float32(7.0) and g == np.float32(384.0)
+
+
+def test_calibration_all_zero_and_empty_give_unit_scale():
+    assert O.calibrate_ref([np.zeros((2, 16))])[1] == np.float32(1.0)
+    assert O.calibrate_ref([])[1] == np.float32(1.0)
+
+
+def test_calibration_is_order_free_and_equals_the_concatenation():
+    rng = np.random.default_rng(11)
+    batches = [rng.standard_t(3, size=(int(rng.integers(1, 9)), 32)).astype(np.float32) for _ in range(7)]
+    _, g = O.calibrate_ref(batches)
+    assert g == O.calibrate_ref(batches[::-1])[1]
+    assert g == O.global_scale(np.concatenate(batches))
+    # and it is the dynamic scale the quantiser would pick for the whole set
+    assert g == np.float32(2688.0) / np.float32(np.abs(np.concatenate(batches)).max())
