@@ -39,9 +39,10 @@ KERNEL_SRCS = {
     "gemm_fast": ("gemm_fast.hip", "gemm_common.h", "nvfp4_device.h"),
     "gemm_decode": ("gemm_decode.hip", "gemm_common.h", "nvfp4_device.h"),
     "amax_observe": ("quantize.hip", "nvfp4_device.h"),
+    "kv_quantize_fp8": ("kv_quantize.hip", "nvfp4_device.h"),
 }
 WORKLOAD_KERNEL = {"gdn": "gemm_fast", "mlp": "gemm_fast", "long": "gemm_fast", "decode": "gemm_decode",
-                   "calib": "amax_observe"}
+                   "calib": "amax_observe", "kv8": "kv_quantize_fp8"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
@@ -50,11 +51,15 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None, help="timed steps (default 50; 1000 for decode)")
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="gdn", choices=["gdn", "mlp", "decode", "long", "calib"],
-                   help="calib: the calibration observer over 32K-token batches (HBM-bound, GB/s)")
+    p.add_argument("--workload", default="gdn", choices=["gdn", "mlp", "decode", "long", "calib", "kv8"],
+                   help="calib: the calibration observer over 32K-token batches; kv8: static FP8 K/V "
+                        "quantisation of a 32K-token context (both HBM-bound, GB/s)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=8192, help="activation rows in the oracle's timed sample")
+    p.add_argument("--fp8-compare", action="store_true",
+                   help="also time an FP8 E4M3 W8A8 GEMM (hipBLASLt through torch._scaled_mm, per-tensor scales, "
+                        "activation cast included) on the same shapes")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain device copy of known size (for HBM counter scaling)")
     return p.parse_args()
@@ -129,6 +134,65 @@ class Prepared:
         return self.m * self.k * self.a.element_size() + self.m * (self.k // 2 + self.k // 16)
 
 
+def fp8_compare(torch, preps, lins, steps, warmup, rotate=1):
+    """The recipes the pages compare against keep these GEMMs in FP8 (the news
+    article, section 04).  Same shapes and inputs: per-tensor E4M3 scales
+    (448 / amax), activation cast to E4M3 every step, weights cast once, bf16
+    output, one hipBLASLt GEMM.  A library baseline, not part of the path."""
+    f8 = getattr(torch, "float8_e4m3fn", None)
+    if f8 is None or not hasattr(torch, "_scaled_mm"):
+        return {"error": "torch has no float8_e4m3fn / _scaled_mm"}
+    res = []
+    try:
+        for lin, p in zip(lins, preps):
+            dev = p.a.device
+            a = p.a.float()
+            w = torch.cat([torch.from_numpy(np.ascontiguousarray(wi, dtype=np.float32)) for _, wi in lin.modules]).to(dev)
+            sa = (a.abs().max() / 448.0).reshape(1).float()
+            sw = (w.abs().max() / 448.0).reshape(1).float()
+            w8s = [(w / sw).to(f8) for _ in range(rotate)]  # copies rotated like the W4A4 weights
+            w8 = w8s[0]
+            a_bf = p.a
+            inv_sa = (1.0 / sa).to(a_bf.dtype)
+            del w, a
+            c = torch.empty((p.m, p.n), dtype=torch.bfloat16, device=dev)
+
+            def one(i):
+                a8 = (a_bf * inv_sa).to(f8)
+                return torch._scaled_mm(a8, w8s[i % rotate].t(), scale_a=sa, scale_b=sw, out_dtype=torch.bfloat16)
+
+            for i in range(warmup):
+                c = one(i)
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for i in range(steps):
+                c = one(i)
+            t1.record()
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1) / steps
+            a8 = (a_bf * inv_sa).to(f8)
+            torch.cuda.synchronize()
+            t0.record()
+            for i in range(steps):
+                c = torch._scaled_mm(a8, w8s[i % rotate].t(), scale_a=sa, scale_b=sw, out_dtype=torch.bfloat16)
+            t1.record()
+            torch.cuda.synchronize()
+            ms_gemm = t0.elapsed_time(t1) / steps
+            fp8_bytes = p.n * p.k + p.m * p.k + p.m * p.n * 2
+            res.append({"name": lin.name, "ms_step": round(ms, 5), "ms_gemm": round(ms_gemm, 5),
+                        "tflops_step": round(p.flops() / (ms * 1e-3) / 1e12, 2),
+                        "tflops_gemm": round(p.flops() / (ms_gemm * 1e-3) / 1e12, 2),
+                        "weight_bytes": p.n * p.k, "gemm_gbs": round(fp8_bytes / (ms_gemm * 1e-3) / 1e9, 1),
+                        "weight_copies_rotated": rotate})
+            del w8, w8s, a8, c
+    except Exception as e:  # a missing FP8 path is reported, not fatal
+        return {"error": f"{type(e).__name__}: {e}"[:300], "done": res}
+    return {"kind": "FP8 E4M3 W8A8, per-tensor scales, hipBLASLt via torch._scaled_mm (library baseline)",
+            "gemms": res, "fp8_mfma_peak_tflops": 5000.0}
+
+
 def copy_calibration(torch):
     """A plain 1 GiB device-to-device copy: the known size that HBM byte
     counters are scaled against."""
@@ -139,6 +203,60 @@ def copy_calibration(torch):
     dst.copy_(src)
     torch.cuda.synchronize()
     return nbytes
+
+
+def run_kv8(args):
+    """Static FP8 KV-cache quantisation: K and V of a 32K-token context, 8 KV
+    heads x 128 (bf16 in, E4M3 out), four layers' worth rotated so the 256 MB
+    Infinity Cache cannot hold them; bytes = 2 read + 1 written per element."""
+    import torch
+
+    import nvfp4_w4a4_block_quantize_amd as nv
+    from nvfp4_w4a4_block_quantize_amd import synth
+
+    nv.load_library()
+    rows, cols, layers = 32768, 1024, 4
+    ins, outs = [], []
+    for i in range(2 * layers):
+        x, _ = synth.activations(args.seed, "long", 800 + i, rows, cols, dist="t3")
+        ins.append(torch.from_numpy(x).cuda().to(torch.bfloat16))
+        outs.append(torch.empty((rows, cols), dtype=torch.uint8, device="cuda:0"))
+        del x
+    state = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    nv.nvfp4_amax_observe(ins[0], state)
+    s = nv.nvfp4_kv_scale_from_amax(state)
+    steps = args.steps if args.steps is not None else 50
+
+    def step(i):
+        j = 2 * (i % layers)
+        nv.nvfp4_kv_quantize_fp8(ins[j], s, out=outs[j])
+        nv.nvfp4_kv_quantize_fp8(ins[j + 1], s, out=outs[j + 1])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    byts = 2 * rows * cols * 3
+    gbs = byts / (ms * 1e-3) / 1e9
+    out = {"metric": "static FP8 KV-cache quantisation GB/s (K and V, 32K tokens), % of HBM roofline",
+           "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16 in, e4m3 out", "data": "synthetic (seeded; no dataset)",
+           "config": {"workload": "kv_fp8_32k_x_8x128", "k_and_v": [rows, cols], "layers_rotated": layers,
+                      "kernel_source_sha": gemm_source_sha("kv8")},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": load_traffic("kv8"),
+                        "kernel": "kv_quantize_kernel", "avg_ms": round(ms / 2, 5)}}
+    if args.copy_calibration:
+        out["copy_calibration_bytes"] = copy_calibration(torch)
+    print(json.dumps(out), flush=True)
 
 
 def run_calib(args):
@@ -277,6 +395,8 @@ def run(args):
         },
         "roofline": roof,
     }
+    if args.fp8_compare:
+        out["fp8_w8a8_compare"] = fp8_compare(torch, preps, lins, min(steps, 200), args.warmup, rotate=rotate)
     if args.copy_calibration:
         out["copy_calibration_bytes"] = copy_calibration(torch)
     if not args.no_cpu_baseline:
@@ -332,6 +452,8 @@ def main():
         sys.exit(2)
     if args.workload == "calib":
         run_calib(args)
+    elif args.workload == "kv8":
+        run_kv8(args)
     else:
         run(args)
 

@@ -122,6 +122,31 @@ nvfp4_status nvfp4_amax_observe(const void* x, int32_t x_dtype, int64_t rows, in
 nvfp4_status nvfp4_gscale_from_amax(const float* amax_state, float* gscale, void* stream);
 
 /*
+ * nvfp4_kv_quantize_fp8 / nvfp4_kv_scale_from_amax — static FP8 quantisation
+ * of attention K/V activations (news article section 03: the "Minima+scales"
+ * variant adds statically calibrated FP8 KV-cache scales; the abstract calls
+ * them performance-free).  Not part of the W4A4 GEMM path; it sits next to
+ * the attention layers.
+ *
+ * nvfp4_kv_quantize_fp8 writes one OCP E4M3FN byte per element:
+ *   out[r][c] = sign(y) | E4M3(|y|),  y = fp32(x[r][c] * s),  s = *scale,
+ * E4M3 rounding to nearest even and saturating at 448 (no NaN produced from
+ * finite input); the dequantised value is e4m3(out) / s.
+ *   x      [rows][ldx] of x_dtype (NVFP4_F32 / BF16 / F16), 16-byte aligned,
+ *          ldx * sizeof(element) a multiple of 16, cols a multiple of 8.
+ *   scale  device fp32[1], the ENCODE scale (448 / calibrated amax).
+ *   out    [rows][cols] bytes, dense, 8-byte aligned (output).
+ * nvfp4_kv_scale_from_amax writes *scale = fp32(448 / amax) (1.0 when amax is
+ * 0) from an amax word filled by nvfp4_amax_observe.  Both device fp32[1].
+ *
+ * Errors: NULL pointers -> ERR_NULL; rows <= 0, cols <= 0, cols % 8 != 0,
+ * ldx < cols -> ERR_SHAPE; alignment -> ERR_ALIGN; bad x_dtype -> ERR_DTYPE.
+ */
+nvfp4_status nvfp4_kv_quantize_fp8(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                   const float* scale, uint8_t* out, void* stream);
+nvfp4_status nvfp4_kv_scale_from_amax(const float* amax_state, float* scale, void* stream);
+
+/*
  * nvfp4_fuse_rescale — checkpoint-side repair of a fused group of separately
  * calibrated modules (news article section 03: bring every tensor of the group
  * to one global scale and fold the ratio into its E4M3 block scales; the

@@ -8,6 +8,8 @@ GPU is visible, the calls raise.
 Functions carry the C names:
   nvfp4_amax_observe(x, amax_state)          -> amax_state
   nvfp4_gscale_from_amax(amax_state)         -> gscale
+  nvfp4_kv_scale_from_amax(amax_state)       -> scale
+  nvfp4_kv_quantize_fp8(x, scale)            -> E4M3 bytes
   nvfp4_quantize(x, gscale, mode)            -> (codes, scales)
   nvfp4_fuse_rescale(scales, k, rows, gs)    -> (g_star, lossy_blocks)
   nvfp4_gemm(a_codes, a_scales, a_gscale,
@@ -39,6 +41,8 @@ SIGNATURES = {
     "nvfp4_gemm": (_I32, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _I32, _I64, _P]),
     "nvfp4_amax_observe": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P]),
     "nvfp4_gscale_from_amax": (_I32, [_P, _P, _P]),
+    "nvfp4_kv_quantize_fp8": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _P]),
+    "nvfp4_kv_scale_from_amax": (_I32, [_P, _P, _P]),
     "nvfp4_status_str": (ctypes.c_char_p, [_I32]),
     "nvfp4_abi_version": (_I32, []),
 }
@@ -149,6 +153,31 @@ def nvfp4_gscale_from_amax(amax_state, gscale=None, stream=None):
                                                _stream_ptr(stream))
     _check("nvfp4_gscale_from_amax", st)
     return gscale
+
+
+def nvfp4_kv_quantize_fp8(x, scale, out=None, stream=None):
+    """Static FP8 E4M3 codes of a 2-D GPU tensor (one byte per element, uint8)."""
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    st = load_library().nvfp4_kv_quantize_fp8(_dev(x, "x"), _dtype_code(x.dtype), rows, cols, x.stride(0),
+                                              _dev(scale, "scale"), _dev(out, "out"), _stream_ptr(stream))
+    _check("nvfp4_kv_quantize_fp8", st)
+    return out
+
+
+def nvfp4_kv_scale_from_amax(amax_state, scale=None, stream=None):
+    """Encode scale fp32(448 / amax) for nvfp4_kv_quantize_fp8."""
+    torch = _torch()
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=amax_state.device)
+    st = load_library().nvfp4_kv_scale_from_amax(_dev(amax_state, "amax_state"), _dev(scale, "scale"),
+                                                 _stream_ptr(stream))
+    _check("nvfp4_kv_scale_from_amax", st)
+    return scale
 
 
 def nvfp4_fuse_rescale(scales, k: int, module_rows, module_gscales, want_lossy: bool = True, stream=None):

@@ -19,7 +19,7 @@ LIB_NAME = "libnvfp4.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 CONFORMANCE_PATH = os.path.join(HERE, "conformance_cvt")
 
-SOURCES = ["nvfp4_abi.cpp", "quantize.hip", "fuse_rescale.hip", "gemm.hip", "gemm_fast.hip", "gemm_decode.hip"]
+SOURCES = ["nvfp4_abi.cpp", "quantize.hip", "fuse_rescale.hip", "gemm.hip", "gemm_fast.hip", "gemm_decode.hip", "kv_quantize.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

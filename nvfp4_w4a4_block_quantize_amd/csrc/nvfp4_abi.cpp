@@ -101,6 +101,29 @@ nvfp4_status nvfp4_gscale_from_amax(const float* amax_state, float* gscale, void
   return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_DEVICE;
 }
 
+nvfp4_status nvfp4_kv_quantize_fp8(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                   const float* scale, uint8_t* out, void* stream) {
+  if (!x || !scale || !out) return NVFP4_ERR_NULL;
+  const int es = dtype_size(x_dtype);
+  if (es == 0) return NVFP4_ERR_DTYPE;
+  if (rows <= 0 || cols <= 0 || cols % 8 != 0 || ldx < cols || rows >= kMaxDim || cols >= kMaxDim ||
+      ldx >= ((int64_t)1 << 40))
+    return NVFP4_ERR_SHAPE;
+  if (!aligned(x, 16) || (ldx * es) % 16 != 0 || !aligned(out, 8) || !aligned(scale, 4)) return NVFP4_ERR_ALIGN;
+  if (!device_ok()) return NVFP4_ERR_DEVICE;
+  const hipError_t e =
+      nvfp4::launch_kv_quantize_fp8(x, x_dtype, rows, cols, ldx, scale, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_DEVICE;
+}
+
+nvfp4_status nvfp4_kv_scale_from_amax(const float* amax_state, float* scale, void* stream) {
+  if (!amax_state || !scale) return NVFP4_ERR_NULL;
+  if (!aligned(amax_state, 4) || !aligned(scale, 4)) return NVFP4_ERR_ALIGN;
+  if (!device_ok()) return NVFP4_ERR_DEVICE;
+  const hipError_t e = nvfp4::launch_kv_scale_from_amax(amax_state, scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_DEVICE;
+}
+
 nvfp4_status nvfp4_fuse_rescale(uint8_t* scales, int64_t k, int32_t n_modules, const int64_t* module_rows,
                                 const float* module_gscales, float* shared_gscale, int64_t* lossy_blocks,
                                 void* stream) {

@@ -18,6 +18,11 @@ hipError_t launch_amax_observe(const void* x, int dtype, int64_t rows, int64_t c
                                hipStream_t stream);
 hipError_t launch_gscale_from_amax(const float* amax_state, float* gscale, hipStream_t stream);
 
+// Static FP8 KV quantisation: out[e] = E4M3(x[e] * *scale), one byte per element.
+hipError_t launch_kv_quantize_fp8(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                  const float* scale, uint8_t* out, hipStream_t stream);
+hipError_t launch_kv_scale_from_amax(const float* amax_state, float* scale, hipStream_t stream);
+
 // Fold rho = g_star / g_module into `count` scale bytes starting at `scales`;
 // adds the number of changed dequantisation factors to *lossy when non-null.
 hipError_t launch_fuse_rescale(uint8_t* scales, int64_t count, float g_star, float g_module, int64_t* lossy,

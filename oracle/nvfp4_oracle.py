@@ -194,6 +194,23 @@ def calibrate_ref(batches):
     return amax, np.float32(GLOBAL_SCALE_NUMERATOR / amax)
 
 
+def kv_scale_ref(amax):
+    """Encode scale of a static FP8 KV cache: fp32(448 / amax), 1.0 for amax = 0
+    (the news article, section 03: statically calibrated FP8 KV-cache scales;
+    448 is the largest finite E4M3 value)."""
+    amax = np.float32(amax)
+    return np.float32(1.0) if amax == 0 else np.float32(np.float32(448.0) / amax)
+
+
+def kv_quantize_ref(x, s):
+    """E4M3FN bytes of y = fp32(x * s): sign bit from y, magnitude rounded to
+    nearest even and saturated at 448 by the same encoder as the block scales."""
+    x = np.asarray(x, dtype=np.float32)
+    y = (x * np.float32(s)).astype(np.float32)
+    mag = e4m3_encode(np.abs(y))
+    return (mag | (np.signbit(y).astype(np.int64) << 7)).astype(np.uint8)
+
+
 def quantize_ref(x, g=None):
     """NVFP4 quantisation of a [rows, cols] array (cols % 16 == 0).
 

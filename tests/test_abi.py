@@ -124,3 +124,16 @@ def test_amax_observe_validation(lib):
     assert lib.nvfp4_gscale_from_amax(None, P, None) == 1
     assert lib.nvfp4_gscale_from_amax(P, None, None) == 1
     assert lib.nvfp4_gscale_from_amax(P + 2, P, None) == 3
+
+
+def test_kv_quantize_validation(lib):
+    kv = lib.nvfp4_kv_quantize_fp8
+    assert kv(None, 1, 4, 32, 32, P, P, None) == 1
+    assert kv(P, 1, 4, 32, 32, None, P, None) == 1
+    assert kv(P, 1, 4, 32, 32, P, None, None) == 1
+    assert kv(P, 9, 4, 32, 32, P, P, None) == 4
+    assert kv(P, 1, 4, 12, 12, P, P, None) == 2
+    assert kv(P, 1, 4, 32, 16, P, P, None) == 2
+    assert kv(P, 1, 4, 32, 32, P, P + 4, None) == 3
+    assert lib.nvfp4_kv_scale_from_amax(None, P, None) == 1
+    assert lib.nvfp4_kv_scale_from_amax(P, P + 1, None) == 3

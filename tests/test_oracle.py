@@ -293,3 +293,35 @@ def test_calibration_is_order_free_and_equals_the_concatenation():
     assert g == O.global_scale(np.concatenate(batches))
     # and it is the dynamic scale the quantiser would pick for the whole set
     assert g == np.float32(2688.0) / np.float32(np.abs(np.concatenate(batches)).max())
+
+
+# ---- static FP8 KV-cache quantisation
+
+def test_kv_fp8_hand_values():
+    # s = 1: exact values, the largest finite value, saturation, signed zero,
+    # subnormal ties (2^-10 -> 0, 3*2^-10 -> the even neighbour 2*2^-9) and a
+    # normal tie (17 lies halfway between 16 = 0x58 and 18 = 0x59 -> 16)
+    x = np.array([1.0, -1.5, 448.0, 500.0, -1e6, -0.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10, 17.0],
+                 dtype=np.float32)
+    q = O.kv_quantize_ref(x, np.float32(1.0))
+    assert list(q) == [0x38, 0xBC, 0x7E, 0x7E, 0xFE, 0x80, 0x01, 0x00, 0x02, 0x58]
+
+
+def test_kv_fp8_matches_torch_cast_in_range():
+    torch = pytest.importorskip("torch")
+    if not hasattr(torch, "float8_e4m3fn"):
+        pytest.skip("torch has no float8_e4m3fn")
+    rng = np.random.default_rng(41)
+    x = (rng.standard_t(3, 200000) * 20).astype(np.float32)
+    s = O.kv_scale_ref(np.abs(x).max())
+    q = O.kv_quantize_ref(x, s)
+    y = (x * s).astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q, ref)  # every |y| <= 448 here: torch's cast is an independent encoder
+
+
+def test_kv_fp8_scale_maps_amax_to_448():
+    assert O.kv_scale_ref(np.float32(7.0)) == np.float32(64.0)
+    assert O.kv_scale_ref(np.float32(0.0)) == np.float32(1.0)
+    x = np.array([-7.0, 3.0], dtype=np.float32)
+    assert O.kv_quantize_ref(x, O.kv_scale_ref(7.0))[0] == 0xFE  # -448
