@@ -28,8 +28,17 @@ __global__ __launch_bounds__(kThreads) void fuse_rescale_kernel(uint8_t* __restr
     changed = (double)f32_from_e4m3(S2) * (double)g_module != (double)d * (double)g_star;
   }
   if (lossy != nullptr) {
+    // one atomic per workgroup: thousands on one address serialise in the L2
+    __shared__ unsigned int wave_count[kThreads / 64];
     const unsigned long long votes = __ballot(changed);
-    if ((threadIdx.x & 63) == 0 && votes != 0ull) atomicAdd(lossy, (unsigned long long)__popcll(votes));
+    if ((threadIdx.x & 63) == 0) wave_count[threadIdx.x >> 6] = (unsigned int)__popcll(votes);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long total = 0;
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w) total += wave_count[w];
+      if (total != 0ull) atomicAdd(lossy, total);
+    }
   }
 }
 
