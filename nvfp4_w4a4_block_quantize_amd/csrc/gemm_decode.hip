@@ -1,4 +1,4 @@
-// Decode-shaped W4A4 GEMM for gfx950 (M <= 32): C = alpha * A_hat W_hat^T on
+// Decode-shaped W4A4 GEMM for gfx950 (M <= 64): C = alpha * A_hat W_hat^T on
 // NVFP4 operands (news article "Qwen3.8-27B最激进4bit量化开源，权重显存暴降2.9倍！",
 // section 02: E2M1 codes, one E4M3 scale per 16 elements, one FP32 global
 // scale per tensor, both operands 4-bit).
@@ -45,7 +45,13 @@ using namespace gemm;
 
 constexpr int kWaves = 4;
 constexpr int kSuperK = 256;  // K elements per super-group: one 128-byte code line per row
-constexpr int kScaleLdsBytes = 32768;  // scale rows staged in LDS when they fit in this
+// LDS bytes for staged scale rows: at least 32 KiB, or all of what the
+// partial-sum reduction takes anyway when that is more
+template <int MT, int T>
+constexpr int scale_lds_bytes() {
+  return kWaves * 16 * MT * (16 * T + 4) * 4 > 32768 ? kWaves * 16 * MT * (16 * T + 4) * 4 : 32768;
+}
+constexpr int64_t kDecodeMaxRows = 64;  // one 64-row block of activations at most
 
 typedef float float4_v __attribute__((ext_vector_type(4)));
 
@@ -82,7 +88,7 @@ struct Super {
 // activation, all of K) are staged in LDS once, with coalesced 16-byte loads,
 // instead of 4 bytes per row and super-group from memory.
 template <int MT, int T, int OCC, bool SL, int OUT>
-__global__ __launch_bounds__(kThreads, OCC) void gemm_decode_kernel(int64_t M, int64_t N, int64_t K,
+__global__ __launch_bounds__(kThreads, OCC) void gemm_decode_kernel(int64_t M_all, int64_t N, int64_t K,
                                                                   const uint8_t* __restrict__ a_codes,
                                                                   const uint8_t* __restrict__ a_scales,
                                                                   const float* __restrict__ a_gscale,
@@ -91,10 +97,19 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_decode_kernel(int64_t M, i
                                                                   const float* __restrict__ w_gscale,
                                                                   void* __restrict__ c, int64_t ldc) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  // blockIdx.y picks a block of 16*MT activation rows (one block when M <= 16*MT;
+  // the blocks stream the same weight rows at about the same time, so all but
+  // the first read of a line come from the caches)
+  const int64_t m0 = (int64_t)blockIdx.y * (16 * MT);
+  const int64_t M = min((int64_t)(16 * MT), M_all - m0);
+  a_codes += m0 * (K / 2);
+  a_scales += m0 * (K / 16);
+  c = static_cast<uint8_t*>(c) + m0 * ldc * (OUT == 0 ? 4 : 2);
   constexpr int R = 16 * T;      // weight rows per workgroup
   constexpr int kPitch = R + 4;  // fp32 words per staged partial row (pad breaks bank aliasing)
   constexpr int kRows = 16 * MT; // activation rows per workgroup
   constexpr int kPartBytes = kWaves * kRows * kPitch * 4;
+  constexpr int kScaleLdsBytes = scale_lds_bytes<MT, T>();
   constexpr int kLdsBytes = SL ? (kPartBytes > kScaleLdsBytes ? kPartBytes : kScaleLdsBytes) : kPartBytes;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   float* const part = reinterpret_cast<float*>(lds);  // [kWaves][kRows * kPitch], after the main loop
@@ -312,9 +327,9 @@ template <int MT, int T, int OCC>
 hipError_t launch_decode_cfg(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                              const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
                              const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream) {
-  const unsigned grid = (unsigned)((n + 16 * T - 1) / (16 * T));
+  const dim3 grid((unsigned)((n + 16 * T - 1) / (16 * T)), (unsigned)((m + 16 * MT - 1) / (16 * MT)));
   // staged scale rows: all of them must fit, and 16-byte loads need 16-byte aligned rows
-  const bool sl = (int64_t)(16 * T + 16 * MT) * (k / 16) <= kScaleLdsBytes &&
+  const bool sl = (int64_t)(16 * T + 16 * MT) * (k / 16) <= scale_lds_bytes<MT, T>() &&
                   (reinterpret_cast<uintptr_t>(a_scales) % 16) == 0 && (reinterpret_cast<uintptr_t>(w_scales) % 16) == 0;
 #define NVFP4_LAUNCH(SLV, OUT)                                                                                     \
   gemm_decode_kernel<MT, T, OCC, SLV, OUT><<<grid, kThreads, 0, stream>>>(m, n, k, a_codes, a_scales, a_gscale, \
@@ -346,7 +361,7 @@ bool gemm_decode_supported(int64_t m, int64_t n, int64_t k, const uint8_t* a_cod
                        (reinterpret_cast<uintptr_t>(w_scales) % 4) == 0;
   // buffer offsets and sizes are 32-bit
   const bool fits = n * (k / 2) < ((int64_t)1 << 31) && m * (k / 2) < ((int64_t)1 << 31);
-  return aligned && fits && m <= 32 && k % kSuperK == 0;
+  return aligned && fits && m <= kDecodeMaxRows && k % kSuperK == 0;
 }
 
 hipError_t launch_gemm_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
@@ -355,7 +370,12 @@ hipError_t launch_gemm_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_
   if (m <= 16)
     return launch_decode_cfg<1, 4, 3>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype,
                                       ldc, stream);
-  return launch_decode_cfg<2, 3, 3>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype,
+  if (m <= 32)
+    return launch_decode_cfg<2, 3, 3>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype,
+                                      ldc, stream);
+  // 64 activation rows: one workgroup reads each weight line once for all of
+  // them; 2 waves per SIMD, since 3 would spill
+  return launch_decode_cfg<4, 3, 2>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype,
                                     ldc, stream);
 }
 

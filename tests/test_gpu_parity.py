@@ -173,13 +173,14 @@ def check_gemm(C, ref, bound, out_dtype):
     assert np.all(C[zero_rows] == 0)
 
 
-# m <= 32 with k % 256 == 0 takes the decode-shaped (weight-streaming) path, k % 512 == 0 with
+# m <= 64 with k % 256 == 0 takes the decode-shaped (weight-streaming) path, k % 512 == 0 with
 # m > 64 the main prefill path (direct-to-LDS), everything else the generic one
 GEMM_SHAPES = [(64, 128, 256), (300, 520, 384), (1, 1, 16), (33, 257, 400), (256, 256, 128), (513, 300, 1056),
                (32, 1000, 640), (7, 333, 48), (64, 96, 4096),
                (16, 4352, 5120), (48, 777, 1024), (1, 300, 192), (32, 129, 64), (64, 33, 128), (32, 4096, 320),
                (33, 520, 2048), (32, 1000, 768), (17, 300, 256), (1, 4099, 1280), (32, 4352, 5120), (31, 100, 2048),
                (32, 520, 17408), (8, 2000, 5120), (32, 700, 6144),
+               (64, 4352, 5120), (57, 300, 8192), (40, 130, 7424), (64, 70, 7680),  # 64-row decode block
                (2048, 8256, 512),  # 264 tiles, a 64-column ragged edge at scale
                (65, 64, 256), (300, 520, 512), (513, 777, 1024), (257, 300, 256), (1000, 1000, 2560), (256, 512, 5120)]
 
