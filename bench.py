@@ -10,8 +10,10 @@ fused by global-scale repair), bf16 output.
 
 Prints one JSON line.  `value` is whole-step TFLOP/s = 2*M*N*K / step time
 (quantisation included); `roofline` covers the dominant kernel (the GEMM),
-timed with HIP events on the stream it runs on; `cpu_baseline` times the CPU
-oracle on a bounded row sample of the same workload.
+launched back to back with HIP events around the loop on the stream it runs
+on, beside the ceilings measured on the chip by the probes library (an
+MFMA-only loop, a streaming read); `cpu_baseline` times the CPU oracle on a
+bounded row sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--workload gdn|mlp|decode|long]
 """
@@ -32,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A4 GEMM TFLOP/s incl. act-quant at 8K-token prefill; % of MFMA/HBM roofline"
 PEAK_F16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_FP4_MFMA_TFLOPS = 10100.0  # MI355X dense fp4 MFMA
 CSRC = os.path.join(ROOT, "nvfp4_w4a4_block_quantize_amd", "csrc")
 # sources of the GEMM kernel each workload's dominant launch runs (traffic counters
 # are tied to these; once they change, the stored counters no longer apply)
@@ -205,6 +208,60 @@ def copy_calibration(torch):
     return nbytes
 
 
+def _probes(torch):
+    """The measurement probes (an MFMA-only loop and a streaming read), built
+    next to the library; None when they are not built."""
+    import ctypes
+
+    path = os.path.join(ROOT, "nvfp4_w4a4_block_quantize_amd", "libnvfp4_probes.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.probe_mfma_f16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+def _time_launches(torch, fn, reps):
+    fn()
+    fn()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / reps
+
+
+def measured_mfma_peak(torch):
+    """fp16 MFMA rate of waves doing nothing but v_mfma_f32_32x32x16_f16
+    (4 waves per SIMD, four independent chains each), TFLOP/s."""
+    lib = _probes(torch)
+    if lib is None:
+        return None
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.current_stream().cuda_stream
+    wg, iters = 2048, 4096
+    ms = _time_launches(torch, lambda: lib.probe_mfma_f16(wg, iters, sink.data_ptr(), st), 5)
+    return wg * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12
+
+
+def measured_stream_read(torch):
+    """HBM read rate of a 1 GiB streaming read with 16-byte non-temporal
+    loads (512 workgroups: the best of a sweep on this chip), GB/s."""
+    lib = _probes(torch)
+    if lib is None:
+        return None
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    buf = torch.ones(1 << 28, dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.current_stream().cuda_stream
+    ms = _time_launches(torch, lambda: lib.probe_stream_read(buf.data_ptr(), buf.numel() * 4, 512, sink.data_ptr(), st), 10)
+    return buf.numel() * 4 / (ms * 1e-3) / 1e9
+
+
 def run_kv8(args):
     """Static FP8 KV-cache quantisation: K and V of a 32K-token context, 8 KV
     heads x 128 (bf16 in, E4M3 out), four layers' worth rotated so the 256 MB
@@ -355,24 +412,52 @@ def run(args):
     q_ms = [float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(n_ev)])) for j in range(len(preps))]
     g_ms = [float(np.mean([evs[i][j][1].elapsed_time(evs[i][j][2]) for i in range(n_ev)])) for j in range(len(preps))]
 
+    # timed region 3: the dominant GEMM alone, back to back (the roofline's
+    # kernel duration; events between kernels add their own overhead to a
+    # decode-sized launch)
+    jd = int(np.argmax([p.flops() for p in preps]))
+    pd = preps[jd]
+    reps = min(steps, 200)
+    state = {"i": 0}
+
+    def gemm_only():
+        wc, ws = pd.copies[state["i"] % len(pd.copies)]
+        state["i"] += 1
+        nv.nvfp4_gemm(pd.ac, pd.asc, pd.ga, wc, ws, pd.gw, out=pd.c)
+
+    dom_ms = _time_launches(torch, gemm_only, reps)
+
     flops = sum(p.flops() for p in preps)
     if args.workload == "decode":
         p = preps[0]
         step_bytes = p.gemm_bytes() + p.quant_bytes() + p.m * (p.k // 2 + p.k // 16)
         value, unit = step_bytes / (ms_step * 1e-3) / 1e9, "GB/s"
-        gb = p.gemm_bytes() / (g_ms[0] * 1e-3) / 1e9
+        gb = p.gemm_bytes() / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gb, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gb / PEAK_HBM_GBS, 4), "traffic": load_traffic(args.workload),
-                "kernel": "nvfp4 gemm (decode shape)", "avg_ms": round(g_ms[0], 5)}
+                "kernel": "nvfp4 gemm (decode shape)", "avg_ms": round(dom_ms, 5)}
+        stream = measured_stream_read(torch)
+        if stream is not None:
+            roof["measured_stream_read_gbs"] = round(stream, 1)
+            roof["frac_of_measured_stream"] = round(gb / stream, 4)
+        # the same call on one weight copy, which then sits in the 256 MB Infinity Cache
+        wc0, ws0 = p.copies[0]
+        ms1 = _time_launches(torch, lambda: nv.nvfp4_gemm(p.ac, p.asc, p.ga, wc0, ws0, p.gw, out=p.c), 200)
+        roof["single_copy_cache_resident_gbs"] = round(p.gemm_bytes() / (ms1 * 1e-3) / 1e9, 1)
         metric = "W4A4 decode-shaped GEMM GB/s incl. act-quant (M=32), % of HBM roofline"
     else:
         value, unit = flops / (ms_step * 1e-3) / 1e12, "TFLOP/s"
         # dominant kernel: the largest GEMM of the step
-        j = int(np.argmax([p.flops() for p in preps]))
-        ach = preps[j].flops() / (g_ms[j] * 1e-3) / 1e12
+        j = jd
+        ach = preps[j].flops() / (dom_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_F16_MFMA_TFLOPS, 4), "traffic": load_traffic(args.workload),
-                "kernel": f"nvfp4 gemm {preps[j].m}x{preps[j].n}x{preps[j].k}", "avg_ms": round(g_ms[j], 5)}
+                "kernel": f"nvfp4 gemm {preps[j].m}x{preps[j].n}x{preps[j].k}", "avg_ms": round(dom_ms, 5),
+                "frac_of_fp4_peak": round(ach / PEAK_FP4_MFMA_TFLOPS, 4)}
+        loop = measured_mfma_peak(torch)
+        if loop is not None:
+            roof["measured_mfma_f16_loop_tflops"] = round(loop, 1)
+            roof["frac_of_measured_loop"] = round(ach / loop, 4)
         metric = METRIC
 
     out = {

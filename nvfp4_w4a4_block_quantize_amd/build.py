@@ -18,6 +18,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libnvfp4.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 CONFORMANCE_PATH = os.path.join(HERE, "conformance_cvt")
+PROBES_PATH = os.path.join(HERE, "libnvfp4_probes.so")
 
 SOURCES = ["nvfp4_abi.cpp", "quantize.hip", "fuse_rescale.hip", "gemm.hip", "gemm_fast.hip", "gemm_decode.hip", "kv_quantize.hip"]
 
@@ -65,8 +66,14 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for conformance_cvt.hip:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     os.replace(CONFORMANCE_PATH + ".tmp", CONFORMANCE_PATH)
+    # measurement probes for the benchmark (MFMA-only loop, streaming read)
+    cmd = [HIPCC, *COMMON_FLAGS, "-shared", os.path.join(CSRC, "probes.hip"), "-o", PROBES_PATH + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for probes.hip:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(PROBES_PATH + ".tmp", PROBES_PATH)
     if verbose:
-        print(f"built {LIB_PATH} and {CONFORMANCE_PATH}")
+        print(f"built {LIB_PATH}, {CONFORMANCE_PATH} and {PROBES_PATH}")
     return LIB_PATH
 
 

@@ -35,6 +35,11 @@
 //  * Decode as in the prefill kernel: v_cvt_scalef32_pk_f16_fp4 (scale 1.0)
 //    then one v_pk_mul_f16 by the E4M3 block scale converted to fp16 (both
 //    exact), products exact in fp32, FP32 accumulation in the MFMA.
+//  * Up to 32 activation rows with K up to about 5.9K, a second kernel keeps
+//    all activation codes and scale rows in LDS: a workgroup of three such
+//    quads of waves (one per CU) stages them once, and its main loop issues
+//    weight loads only.  Larger M or K, or operands off a 16-byte boundary,
+//    take the first kernel (64 rows at most).
 #include "gemm_common.h"
 #include "nvfp4_internal.h"
 
@@ -54,6 +59,7 @@ constexpr int scale_lds_bytes() {
 constexpr int64_t kDecodeMaxRows = 64;  // one 64-row block of activations at most
 
 typedef float float4_v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 #if defined(__HIP_DEVICE_COMPILE__)
 
@@ -80,6 +86,42 @@ struct Super {
   Frag w[T];
   Frag a[MT];
 };
+
+// four consecutive outputs of row m from column n on (columns past N dropped)
+template <int OUT>
+__device__ __forceinline__ void store_run4(void* c, int64_t ldc, int64_t m, int64_t n, int64_t N, const float (&o)[4],
+                                           bool vec_ok) {
+  if constexpr (OUT == 0) {
+    float* p = static_cast<float*>(c) + m * ldc + n;
+    if (n + 3 < N && vec_ok) {
+      *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < N) p[e] = o[e];
+    }
+  } else {
+    uint16_t* p = static_cast<uint16_t*>(c) + m * ldc + n;
+    uint16_t b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (OUT == 1) {
+        b[e] = (uint16_t)bf16_rne_bits(o[e]);
+      } else {
+        const _Float16 hv = (_Float16)o[e];
+        __builtin_memcpy(&b[e], &hv, 2);
+      }
+    }
+    if (n + 3 < N && (reinterpret_cast<uintptr_t>(p) % 8) == 0) {
+      *reinterpret_cast<uint2*>(p) = make_uint2((uint32_t)b[0] | ((uint32_t)b[1] << 16),
+                                                (uint32_t)b[2] | ((uint32_t)b[3] << 16));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < N) p[e] = b[e];
+    }
+  }
+}
 
 #endif  // __HIP_DEVICE_COMPILE__
 
@@ -289,38 +331,264 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_decode_kernel(int64_t M_al
     for (int w = 1; w < kWaves; ++w)
       s += *reinterpret_cast<const float4_v*>(part + w * (kRows * kPitch) + row * kPitch + 4 * run);
     const float o[4] = {s[0] * alpha, s[1] * alpha, s[2] * alpha, s[3] * alpha};
-    if constexpr (OUT == 0) {
-      float* p = static_cast<float*>(c) + m * ldc + n;
-      if (n + 3 < N && vec_ok) {
-        *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (n + e < N) p[e] = o[e];
-      }
-    } else {
-      uint16_t* p = static_cast<uint16_t*>(c) + m * ldc + n;
-      uint16_t b[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (OUT == 1) {
-          b[e] = (uint16_t)bf16_rne_bits(o[e]);
-        } else {
-          const _Float16 hv = (_Float16)o[e];
-          __builtin_memcpy(&b[e], &hv, 2);
-        }
-      }
-      if (n + 3 < N && (reinterpret_cast<uintptr_t>(p) % 8) == 0) {
-        *reinterpret_cast<uint2*>(p) = make_uint2((uint32_t)b[0] | ((uint32_t)b[1] << 16),
-                                                  (uint32_t)b[2] | ((uint32_t)b[3] << 16));
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (n + e < N) p[e] = b[e];
-      }
-    }
+    store_run4<OUT>(c, ldc, m, n, N, o, vec_ok);
   }
 #endif
+}
+
+// ---------------------------------------------------------------------------
+// Activations resident in LDS.  A wave's vector loads complete in issue
+// order, so in the kernel above an activation fragment load (an L2 hit)
+// issued behind weight loads holds its place until those come back from HBM:
+// two in five of the loads in flight carry no HBM bytes.  Here a workgroup of
+// Q quads (four waves each; each quad owns one group of R = 16*T weight rows
+// over all of K, as a workgroup above does) first copies all activation codes
+// and every scale row it uses into LDS, once, with coalesced 16-byte loads.
+// The main loop then issues weight loads only and reads the activation
+// fragments from LDS.  Q quads share one copy of A, so A is read from L2 Q
+// times less often as well.
+constexpr int kAlLdsBytes = 160 * 1024;  // all of a CU's LDS: one workgroup per CU
+constexpr int kAlPad = 16;  // bytes added to each staged row: rows r and r+1 start 4 banks apart
+constexpr int kAlT = 3, kAlQ = 3;  // 3 weight tiles per quad, 3 quads (12 waves) per workgroup
+constexpr int kAlD = 2;  // super-groups of weight loads in flight per wave
+constexpr int64_t kAlRowsPerWg = 16 * kAlT * kAlQ;
+
+template <int MT, int T, int Q, int D, int OUT>
+__global__ __launch_bounds__(kThreads * Q, Q) void gemm_decode_al_kernel(int64_t M, int64_t N, int64_t K,
+                                                                      const uint8_t* __restrict__ a_codes,
+                                                                      const uint8_t* __restrict__ a_scales,
+                                                                      const float* __restrict__ a_gscale,
+                                                                      const uint8_t* __restrict__ w_codes,
+                                                                      const uint8_t* __restrict__ w_scales,
+                                                                      const float* __restrict__ w_gscale,
+                                                                      void* __restrict__ c, int64_t ldc) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int R = 16 * T;       // weight rows per quad
+  constexpr int kRows = 16 * MT;  // activation rows
+  constexpr int kPitch = R + 4;   // fp32 words per staged partial row
+  constexpr int kPartBytes = kWaves * kRows * kPitch * 4;  // one quad's partial sums
+  static_assert(Q * kPartBytes <= kAlLdsBytes, "partial sums fit");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kAlLdsBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qd = wave >> 2, wv = wave & 3;  // quad, wave within the quad
+  const int lr = lane & 15, q = lane >> 4;
+  const int64_t wg_row0 = (int64_t)blockIdx.x * (Q * R);
+  const int64_t n0 = wg_row0 + qd * R;
+
+  const int64_t code_ld = K / 2, scale_ld = K / 16;
+  const int apitch = (int)code_ld + kAlPad;   // LDS bytes per activation code row
+  const int spitch = (int)scale_ld + kAlPad;  // LDS bytes per scale row
+  // LDS: activation codes [kRows][apitch], then scale rows [Q*R weight rows,
+  // quad-major, then kRows activation rows][spitch]; after the main loop the
+  // quads' partial sums overwrite the front
+  uint8_t* const lds_a = lds;
+  uint8_t* const lds_s = lds + kRows * apitch;
+
+  const __amdgpu_buffer_rsrc_t wc_r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)w_codes, (short)0, (int)(N * code_ld), 0x00020000);
+  uint32_t wc_off[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    int64_t r = n0 + 16 * t + lr;
+    r = r < N ? r : N - 1;
+    wc_off[t] = (uint32_t)(r * code_ld + 32 * q);
+  }
+
+  const int G = (int)(K / kSuperK);
+  const int ng = (G - wv + kWaves - 1) / kWaves;
+  auto gidx = [&](int jj) { return wv + kWaves * jj; };
+
+  // one weight tile's code bytes of a super-group (32 per lane)
+  struct WCodes {
+    uint4 c[2];
+  };
+  auto load_w = [&](WCodes (&b)[T], int g) {
+    g = max(0, min(g, G - 1));
+    const int cs = g * (kSuperK / 2);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      b[t].c[0] = load16(wc_r, wc_off[t], cs);
+      b[t].c[1] = load16(wc_r, wc_off[t], cs + 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  float4_v acc[MT][T];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[i][t] = float4_v{0.f, 0.f, 0.f, 0.f};
+
+  // super-group g: activation fragments and all scale words from LDS, then
+  // 8 MFMA steps per weight tile and activation tile
+  auto compute = [&](const WCodes (&bw)[T], int g) {
+    Frag a[MT];
+    uint32_t ws[T];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const uint8_t* pa = lds_a + (16 * i + lr) * apitch + g * (kSuperK / 2) + 32 * q;
+      a[i].c[0] = *reinterpret_cast<const uint4*>(pa);
+      a[i].c[1] = *reinterpret_cast<const uint4*>(pa + 16);
+      a[i].s = *reinterpret_cast<const uint32_t*>(lds_s + (Q * R + 16 * i + lr) * spitch + g * 16 + 4 * q);
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      ws[t] = *reinterpret_cast<const uint32_t*>(lds_s + (qd * R + 16 * t + lr) * spitch + g * 16 + 4 * q);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      auto scale_of = [&](uint32_t w) {
+        const half2_t sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w >> (16 * (s >> 2)), 1.0f, false);
+        const _Float16 v = sp[(s >> 1) & 1];
+        return half2_t{v, v};
+      };
+      half8_t fa[MT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) fa[i] = decode8(word_at(a[i].c, s), scale_of(a[i].s));
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const half8_t fw = decode8(word_at(bw[t].c, s), scale_of(ws[t]));
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw, fa[i], acc[i][t], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // Staging, in three segments of 16-byte chunks: activation code rows,
+  // weight scale rows, activation scale rows.  Chunk f of a segment is row
+  // f / cpr, chunk f % cpr (a multiply with ceil(2^32 / cpr): exact while
+  // f * cpr < 2^32); rows past M or N repeat the last row (never stored) and
+  // threads past the end repeat the segment's last chunk (same bytes to the
+  // same place).  One batch of loads covers all three segments for K up to
+  // 6144; every staging load goes out before the weight loads (loads
+  // complete in issue order: the staging data is not held behind HBM
+  // latency), and a chunk loop covers what a batch misses.
+  constexpr int TH = kThreads * Q;
+  constexpr int UA = 4 * MT, UW = (Q * R * 24 + TH - 1) / TH, US = (kRows * 24 + TH - 1) / TH;
+  const int cpr_a = (int)(code_ld / 16), cpr_s = (int)(scale_ld / 16);
+  const int n_a = kRows * cpr_a, n_w = Q * R * cpr_s, n_s = kRows * cpr_s;
+  // ceil(2^32 / cpr) = floor((2^32 - 1) / cpr) + 1, by a 32-bit division
+  const uint64_t mag_a = (uint64_t)(0xFFFFFFFFu / (uint32_t)cpr_a) + 1;
+  const uint64_t mag_s = (uint64_t)(0xFFFFFFFFu / (uint32_t)cpr_s) + 1;
+  auto row_of = [](int f, uint64_t mag) { return (int)(((uint64_t)(uint32_t)f * mag) >> 32); };
+  // segment chunk f -> source address and LDS offset
+  auto a_src = [&](int f) {
+    const int r = row_of(f, mag_a), ch = f - r * cpr_a;
+    return a_codes + min((int64_t)r, M - 1) * code_ld + 16 * ch;
+  };
+  auto a_dst = [&](int f) {
+    const int r = row_of(f, mag_a);
+    return r * apitch + 16 * (f - r * cpr_a);
+  };
+  auto w_src = [&](int f) {
+    const int r = row_of(f, mag_s), ch = f - r * cpr_s;
+    return w_scales + min(wg_row0 + r, N - 1) * scale_ld + 16 * ch;
+  };
+  auto s_src = [&](int f) {
+    const int r = row_of(f, mag_s), ch = f - r * cpr_s;
+    return a_scales + min((int64_t)r, M - 1) * scale_ld + 16 * ch;
+  };
+  auto sc_dst = [&](int row0, int f) {  // scale segment starting at scale row row0
+    const int r = row_of(f, mag_s);
+    return kRows * apitch + (row0 + r) * spitch + 16 * (f - r * cpr_s);
+  };
+
+  WCodes b[D][T];
+  {
+    u32x4_t va[UA], vw[UW], vs[US];
+#pragma unroll
+    for (int u = 0; u < UA; ++u) va[u] = *reinterpret_cast<const u32x4_t*>(a_src(min(u * TH + tid, n_a - 1)));
+#pragma unroll
+    for (int u = 0; u < UW; ++u) vw[u] = *reinterpret_cast<const u32x4_t*>(w_src(min(u * TH + tid, n_w - 1)));
+#pragma unroll
+    for (int u = 0; u < US; ++u) vs[u] = *reinterpret_cast<const u32x4_t*>(s_src(min(u * TH + tid, n_s - 1)));
+    load_w(b[0], gidx(0));
+#pragma unroll
+    for (int u = 0; u < UA; ++u) *reinterpret_cast<u32x4_t*>(lds + a_dst(min(u * TH + tid, n_a - 1))) = va[u];
+#pragma unroll
+    for (int u = 0; u < UW; ++u) *reinterpret_cast<u32x4_t*>(lds + sc_dst(0, min(u * TH + tid, n_w - 1))) = vw[u];
+#pragma unroll
+    for (int u = 0; u < US; ++u) *reinterpret_cast<u32x4_t*>(lds + sc_dst(Q * R, min(u * TH + tid, n_s - 1))) = vs[u];
+  }
+  for (int f = UA * TH + tid; f < n_a; f += TH)
+    *reinterpret_cast<u32x4_t*>(lds + a_dst(f)) = *reinterpret_cast<const u32x4_t*>(a_src(f));
+  for (int f = UW * TH + tid; f < n_w; f += TH)
+    *reinterpret_cast<u32x4_t*>(lds + sc_dst(0, f)) = *reinterpret_cast<const u32x4_t*>(w_src(f));
+  for (int f = US * TH + tid; f < n_s; f += TH)
+    *reinterpret_cast<u32x4_t*>(lds + sc_dst(Q * R, f)) = *reinterpret_cast<const u32x4_t*>(s_src(f));
+  // the other super-groups' weight loads once the staging registers are free
+#pragma unroll
+  for (int d = 1; d < D; ++d) load_w(b[d], gidx(min(d, max(ng - 1, 0))));
+  __syncthreads();
+
+  // D super-groups of weight loads in flight per wave
+  int j = 0;
+  for (; j + D <= ng; j += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      compute(b[d], gidx(j + d));
+      load_w(b[d], gidx(min(j + d + D, ng - 1)));
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d)
+    if (j + d < ng) compute(b[d], gidx(j + d));
+  // (weight loads issued past a wave's last super-group only target registers)
+  __syncthreads();  // every quad is done reading the staged rows
+
+  float* const part = reinterpret_cast<float*>(lds + qd * kPartBytes);  // [kWaves][kRows * kPitch]
+  float* mine = part + wv * (kRows * kPitch);
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      *reinterpret_cast<float4_v*>(mine + (16 * i + lr) * kPitch + 16 * t + 4 * q) = acc[i][t];
+  __syncthreads();
+
+  const float alpha = 1.0f / (*a_gscale * *w_gscale);
+  constexpr int kRuns = R / 4;
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(c) % 16) == 0 && (ldc * (OUT == 0 ? 4 : 2)) % 16 == 0;
+  for (int f = tid & (kThreads - 1); f < kRows * kRuns; f += kThreads) {
+    const int row = f / kRuns, run = f % kRuns;
+    const int64_t n = n0 + 4 * run;
+    if (row >= M || n >= N) continue;
+    float4_v s = *reinterpret_cast<const float4_v*>(part + row * kPitch + 4 * run);
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w)
+      s += *reinterpret_cast<const float4_v*>(part + w * (kRows * kPitch) + row * kPitch + 4 * run);
+    const float o[4] = {s[0] * alpha, s[1] * alpha, s[2] * alpha, s[3] * alpha};
+    store_run4<OUT>(c, ldc, row, n, N, o, vec_ok);
+  }
+#endif
+}
+
+// LDS bytes the kernel above stages for these sizes
+template <int MT, int T, int Q>
+constexpr int64_t al_lds_bytes(int64_t k) {
+  return (int64_t)(16 * MT) * (k / 2 + kAlPad) + (int64_t)(Q * 16 * T + 16 * MT) * (k / 16 + kAlPad);
+}
+
+// D super-groups of weight loads in flight per wave
+template <int MT, int T, int Q, int D>
+hipError_t launch_decode_al(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
+                            const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
+                            const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream) {
+  const dim3 grid((unsigned)((n + Q * 16 * T - 1) / (Q * 16 * T)));
+#define NVFP4_LAUNCH_AL(OUT)                                                                                 \
+  gemm_decode_al_kernel<MT, T, Q, D, OUT><<<grid, kThreads * Q, 0, stream>>>(m, n, k, a_codes, a_scales, \
+                                                                               a_gscale, w_codes, w_scales, \
+                                                                               w_gscale, c, ldc)
+  if (out_dtype == 0)
+    NVFP4_LAUNCH_AL(0);
+  else if (out_dtype == 1)
+    NVFP4_LAUNCH_AL(1);
+  else
+    NVFP4_LAUNCH_AL(2);
+#undef NVFP4_LAUNCH_AL
+  return hipGetLastError();
 }
 
 template <int MT, int T, int OCC>
@@ -367,6 +635,25 @@ bool gemm_decode_supported(int64_t m, int64_t n, int64_t k, const uint8_t* a_cod
 hipError_t launch_gemm_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                               const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
                               const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream) {
+  // up to 32 activation rows: the activations resident in LDS when they fit
+  // (K up to about 5.9K), with 16-byte staging loads, and when one workgroup
+  // per CU covers N in a single round (a second, partial round would cost
+  // more than the kernel saves)
+  const bool al_ok = (reinterpret_cast<uintptr_t>(a_codes) % 16) == 0 &&
+                     (reinterpret_cast<uintptr_t>(a_scales) % 16) == 0 &&
+                     (reinterpret_cast<uintptr_t>(w_scales) % 16) == 0 && m <= 32 &&
+                     (n + kAlRowsPerWg - 1) / kAlRowsPerWg <= device_cu_count();
+#define NVFP4_AL(MT)                                                                                           \
+  if (al_lds_bytes<MT, kAlT, kAlQ>(k) <= kAlLdsBytes)                                                          \
+    return launch_decode_al<MT, kAlT, kAlQ, kAlD>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales,   \
+                                                  w_gscale, c, out_dtype, ldc, stream);
+  if (al_ok && m <= 16) {
+    NVFP4_AL(1)
+  }
+  if (al_ok) {
+    NVFP4_AL(2)
+  }
+#undef NVFP4_AL
   if (m <= 16)
     return launch_decode_cfg<1, 4, 3>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype,
                                       ldc, stream);

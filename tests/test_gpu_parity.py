@@ -181,6 +181,7 @@ GEMM_SHAPES = [(64, 128, 256), (300, 520, 384), (1, 1, 16), (33, 257, 400), (256
                (33, 520, 2048), (32, 1000, 768), (17, 300, 256), (1, 4099, 1280), (32, 4352, 5120), (31, 100, 2048),
                (32, 520, 17408), (8, 2000, 5120), (32, 700, 6144),
                (64, 4352, 5120), (57, 300, 8192), (40, 130, 7424), (64, 70, 7680),  # 64-row decode block
+               (9, 200, 9216), (5, 130, 17408), (24, 1100, 6144), (3, 9000, 4096), (12, 37000, 512),  # LDS-resident A or not
                (2048, 8256, 512),  # 264 tiles, a 64-column ragged edge at scale
                (65, 64, 256), (300, 520, 512), (513, 777, 1024), (257, 300, 256), (1000, 1000, 2560), (256, 512, 5120)]
 
@@ -197,6 +198,36 @@ def test_gemm_random_codes(gpu_lib, shape, out_dtype):
     C = gemm_gpu(gpu_lib, ac, asc, ga, wc, wsc, gw, out_dtype)
     ref, bound = O.gemm_ref(ac, asc, ga, wc, wsc, gw)
     check_gemm(C, ref, bound, out_dtype)
+
+
+@pytest.mark.parametrize("shape", [(20, 700, 1024), (9, 300, 2048), (32, 500, 5120), (50, 260, 1536), (100, 300, 1024)])
+@pytest.mark.parametrize("scale_offset", [0, 4, 1])
+def test_gemm_offset_scales_strided_output(gpu_lib, shape, scale_offset):
+    """Scale operands off a 16-byte boundary (legal: the ABI puts no alignment
+    on scales) take the paths that load scales from memory, or the generic
+    kernel at a byte offset; outputs go to an odd row stride, and the columns
+    past n stay untouched."""
+    M, N, K = shape
+    rng = np.random.default_rng([28, M, N, K, scale_offset])
+    ac, asc = rand_operand(rng, M, K)
+    wc, wsc = rand_operand(rng, N, K)
+    ga, gw = np.float32(rng.uniform(0.5, 300)), np.float32(rng.uniform(100, 3e4))
+    log("gemm offset/strided", shape, scale_offset)
+
+    def dev_at(a, off):
+        flat = torch.zeros(a.size + 64, dtype=torch.uint8, device="cuda")
+        flat[off:off + a.size] = torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).cuda()
+        return flat[off:off + a.size].view(a.shape)
+
+    ldc = N + 37
+    big = torch.full((M, ldc), 7.0, dtype=torch.float32, device="cuda")
+    out = big[:, :N]
+    gpu_lib.nvfp4_gemm(dev_at(ac, 0), dev_at(asc, scale_offset), gscale_tensor(ga), dev_at(wc, 0),
+                       dev_at(wsc, scale_offset), gscale_tensor(gw), out=out)
+    torch.cuda.synchronize()
+    ref, bound = O.gemm_ref(ac, asc, ga, wc, wsc, gw)
+    check_gemm(out.cpu().numpy(), ref, bound, "f32")
+    assert torch.all(big[:, N:] == 7.0).item(), "columns past n were written"
 
 
 def test_gemm_f16_output(gpu_lib):

@@ -121,3 +121,50 @@ def test_workload_full_size(gpu_lib, config):
         log("workload", config, lin.name, lin.a.shape, "x", lin.n)
         worst = run_linear(gpu_lib, lin, rng)
         log("workload", config, lin.name, "max err/bound", worst)
+
+
+@pytest.mark.parametrize("config", ["gdn", "decode"])
+def test_workload_full_tensor_bytes(gpu_lib, config):
+    """Every code and scale byte of the workload's quantised operands against the
+    oracle, not samples: the activation under its calibrated static scale, each
+    weight module under its own dynamic scale, and the scales after the
+    global-scale repair of the fused modules."""
+    nv = gpu_lib
+    dev = torch.device("cuda:0")
+    log("full tensor", config, "generating inputs")
+    lin = synth.make_workload(config, seed=0)[0]
+    m, k = lin.a.shape
+    ga = torch.zeros(1, dtype=torch.float32, device=dev)
+    nv.nvfp4_quantize(to_dev(lin.a_calib, lin.a_dtype), ga, "dynamic")
+    ac, asc = nv.nvfp4_quantize(to_dev(lin.a, lin.a_dtype), ga, "static")
+    g_a = O.global_scale(lin.a_calib)
+    assert np.float32(ga.item()) == g_a
+    log("full tensor", config, "activation", (m, k))
+    for r0 in range(0, m, 2048):
+        rc, rs, _ = O.quantize_ref(lin.a[r0:r0 + 2048], g_a)
+        assert np.array_equal(ac[r0:r0 + 2048].cpu().numpy(), rc), f"activation codes, rows {r0}+"
+        assert np.array_equal(asc[r0:r0 + 2048].cpu().numpy(), rs), f"activation scales, rows {r0}+"
+
+    ws = torch.empty((lin.n, k // 16), dtype=torch.uint8, device=dev)
+    wc = torch.empty((lin.n, k // 2), dtype=torch.uint8, device=dev)
+    gs, rows, ref_scales, r0 = [], [], [], 0
+    for name, w in lin.modules:
+        g = torch.zeros(1, dtype=torch.float32, device=dev)
+        nv.nvfp4_quantize(to_dev(w, lin.a_dtype), g, "dynamic", codes=wc[r0:r0 + w.shape[0]], scales=ws[r0:r0 + w.shape[0]])
+        g_i = O.global_scale(w)
+        assert np.float32(g.item()) == g_i, name
+        log("full tensor", config, name, w.shape)
+        for q0 in range(0, w.shape[0], 4096):
+            rc, rs, _ = O.quantize_ref(w[q0:q0 + 4096], g_i)
+            assert np.array_equal(wc[r0 + q0:r0 + q0 + rc.shape[0]].cpu().numpy(), rc), f"{name} codes, rows {q0}+"
+            assert np.array_equal(ws[r0 + q0:r0 + q0 + rc.shape[0]].cpu().numpy(), rs), f"{name} scales, rows {q0}+"
+            ref_scales.append(rs)
+        gs.append(float(g.item()))
+        rows.append(w.shape[0])
+        r0 += w.shape[0]
+    if len(rows) > 1:
+        g_star, lossy = nv.nvfp4_fuse_rescale(ws, k, rows, gs)
+        folded, ref_gstar, ref_lossy = O.fuse_rescale_ref(np.concatenate(ref_scales), rows, gs)
+        assert np.float32(g_star) == ref_gstar
+        assert int(lossy.item()) == ref_lossy
+        assert np.array_equal(ws.cpu().numpy(), folded), "fused scales"
