@@ -194,13 +194,18 @@ nvfp4_status nvfp4_fuse_rescale(uint8_t* scales, int64_t k, int32_t n_modules, c
  *   w_codes  [n][k/2], w_scales [n][k/16], w_gscale device fp32[1]
  *   c        [m][ldc] of c_dtype (NVFP4_F32, NVFP4_BF16 or NVFP4_F16), only
  *            the first n columns of each row are written; ldc >= n.
- *   Alignment: codes 16-byte aligned; c aligned to its element size.
+ *   Alignment: codes 16-byte aligned; c aligned to its element size.  Scales
+ *            need no alignment; the prefill and decode-shaped kernels take
+ *            4-byte aligned scale pointers (others go to a generic kernel),
+ *            and the decode-shaped kernels stage scale rows in LDS with
+ *            16-byte loads when the pointers are 16-byte aligned.
  *
  * Every decoded operand e2m1*e4m3 is exact in fp16 (at most 6 significant
  * bits, magnitudes 2^-10 .. 2688), every product is exact in fp32 and the sum
- * is accumulated in fp32; the summation order is fixed for a given shape, so
- * results are deterministic.  bf16/f16 outputs are the fp32 result rounded to
- * nearest even.
+ * is accumulated in fp32.  The kernel, and with it the summation order, is
+ * chosen from the shape, the operands' alignment and the device's CU count;
+ * for a given choice it is fixed, so repeated calls give identical results.
+ * bf16/f16 outputs are the fp32 result rounded to nearest even.
  *
  * Errors: NULL pointers -> ERR_NULL; m, n, k <= 0, k % 16 != 0, ldc < n ->
  * ERR_SHAPE; alignment -> ERR_ALIGN; bad c_dtype -> ERR_DTYPE.
