@@ -9,6 +9,8 @@
 //  3. v_cvt_scalef32_pk_f16_fp8 with scale 1.0 (GEMM block scales) and
 //     v_cvt_f32_fp8 (quantiser): each of the 254 finite E4M3FN bytes gives its
 //     exact value (bias 7, subnormals m * 2^-9).
+//  4. v_cvt_pk_bf16_f32 (GEMM epilogue, bf16 output): fp32 to bf16 nearest,
+//     ties to even, compared for every non-NaN fp32 bit pattern.
 //
 // Prints one line per check and exits 0 only when every count of mismatches
 // is zero.  Built next to the library; run by the GPU test suite.
@@ -52,6 +54,25 @@ __global__ void check_fp4_encode(unsigned long long* bad) {
 }
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// bf16 nearest-even of a finite or infinite fp32: add half a unit of the
+// 16 dropped bits (less one when the kept part is even) and truncate
+__device__ uint32_t bf16_rule(uint32_t u) { return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16; }
+
+__global__ void check_bf16_pack(unsigned long long* bad) {
+  unsigned long long nb = 0;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 32); i += 2 * stride) {
+    const uint32_t u0 = (uint32_t)i;
+    const uint32_t u1 = (uint32_t)(i + stride);  // i + stride < 2^32: i < 2^32 - 2*stride at every step
+    const bf16x2_t v = {(__bf16)__uint_as_float(u0), (__bf16)__uint_as_float(u1)};
+    const uint32_t hw = __builtin_bit_cast(uint32_t, v);
+    if ((u0 & 0x7FFFFFFFu) <= 0x7F800000u && (hw & 0xFFFFu) != bf16_rule(u0)) ++nb;
+    if ((u1 & 0x7FFFFFFFu) <= 0x7F800000u && (hw >> 16) != bf16_rule(u1)) ++nb;
+  }
+  if (nb) atomicAdd(bad, nb);
+}
 
 __global__ void check_decodes(unsigned long long* bad) {
   const uint32_t t = threadIdx.x;  // 0..255
@@ -72,15 +93,17 @@ __global__ void check_decodes(unsigned long long* bad) {
 
 int main() {
   unsigned long long* bad = nullptr;
-  if (hipMalloc(&bad, 2 * sizeof(unsigned long long)) != hipSuccess) return 2;
-  if (hipMemset(bad, 0, 2 * sizeof(unsigned long long)) != hipSuccess) return 2;
+  if (hipMalloc(&bad, 3 * sizeof(unsigned long long)) != hipSuccess) return 2;
+  if (hipMemset(bad, 0, 3 * sizeof(unsigned long long)) != hipSuccess) return 2;
   check_fp4_encode<<<4096, 256>>>(bad);
   check_decodes<<<1, 256>>>(bad + 1);
-  unsigned long long h[2] = {1, 1};
+  check_bf16_pack<<<4096, 256>>>(bad + 2);
+  unsigned long long h[3] = {1, 1, 1};
   if (hipDeviceSynchronize() != hipSuccess) return 2;
   if (hipMemcpy(h, bad, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return 2;
   printf("fp4 encode (all non-NaN fp32 inputs): %llu mismatches\n", h[0]);
   printf("fp4->f16, e4m3->f16, e4m3->f32 decodes (all codes): %llu mismatches\n", h[1]);
+  printf("fp32->bf16 pack (all non-NaN fp32 inputs): %llu mismatches\n", h[2]);
   hipFree(bad);
-  return (h[0] == 0 && h[1] == 0) ? 0 : 1;
+  return (h[0] == 0 && h[1] == 0 && h[2] == 0) ? 0 : 1;
 }

@@ -61,6 +61,15 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// two fp32 values to bf16, nearest even, packed low/high: one
+// v_cvt_pk_bf16_f32 (equal to bf16_rne_bits on every non-NaN input; the
+// conformance program checks all of them)
+__device__ __forceinline__ uint32_t bf16x2_rne_bits(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 template <int OUT>
 __device__ __forceinline__ void store_out(void* c, int64_t idx, float v) {
   if constexpr (OUT == 0) {

@@ -103,11 +103,15 @@ __device__ __forceinline__ void store_run4(void* c, int64_t ldc, int64_t m, int6
   } else {
     uint16_t* p = static_cast<uint16_t*>(c) + m * ldc + n;
     uint16_t b[4];
+    if constexpr (OUT == 1) {
+      const uint32_t lo = bf16x2_rne_bits(o[0], o[1]), hi = bf16x2_rne_bits(o[2], o[3]);
+      b[0] = (uint16_t)lo;
+      b[1] = (uint16_t)(lo >> 16);
+      b[2] = (uint16_t)hi;
+      b[3] = (uint16_t)(hi >> 16);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if constexpr (OUT == 1) {
-        b[e] = (uint16_t)bf16_rne_bits(o[e]);
-      } else {
+      for (int e = 0; e < 4; ++e) {
         const _Float16 hv = (_Float16)o[e];
         __builtin_memcpy(&b[e], &hv, 2);
       }

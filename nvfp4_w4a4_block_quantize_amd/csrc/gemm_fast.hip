@@ -262,7 +262,7 @@ struct Tile {
 template <int OUT>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   if constexpr (OUT == 1) {
-    return bf16_rne_bits(a) | (bf16_rne_bits(b) << 16);
+    return bf16x2_rne_bits(a, b);
   } else {
     const _Float16 ha = (_Float16)a, hb = (_Float16)b;
     uint16_t ua, ub;
