@@ -360,6 +360,29 @@ def check_sign_symmetry(quantize, seed=10):
     return int(np.count_nonzero((np.asarray(a[0]) ^ 0x88) != np.asarray(b[0]))) + int(np.count_nonzero(np.asarray(a[1]) != np.asarray(b[1])))
 
 
+def check_idempotence(quantize, dequant, seed=11):
+    """With a power-of-two global scale, quantising the dequantised tensor
+    again gives back the same bytes on every block whose E4M3 scale is a
+    normal value.  Such a block holds a code of magnitude 6, so its amax is
+    6 dec(S)/g exactly and the scale comes back unchanged, and every element
+    already sits on the E2M1 grid (saturated blocks included)."""
+    rng = np.random.default_rng(seed)
+    bad = 0
+    for g in (np.float32(1.0), np.float32(64.0), np.float32(0.125)):
+        x = (rng.standard_normal((16, 128)) * rng.uniform(0.01, 50.0, (16, 1))).astype(np.float32)
+        x[3, 16:32] = -0.0
+        codes, scales, _ = quantize(x, g)
+        codes, scales = np.asarray(codes), np.asarray(scales)
+        xh = np.asarray(dequant(codes, scales, g), dtype=np.float64).astype(np.float32)
+        c2, s2, _ = quantize(xh, g)
+        c2, s2 = np.asarray(c2), np.asarray(s2)
+        normal = (scales & 0x7F) >= 0x08  # [rows, blocks]
+        bad += int(np.count_nonzero(normal & (s2 != scales)))
+        same_codes = (c2 == codes).reshape(codes.shape[0], -1, 8).all(axis=2)  # 8 bytes per block
+        bad += int(np.count_nonzero(normal & ~same_codes))
+    return bad
+
+
 def check_underflowed_blocks_are_zero(quantize, seed=17):
     """A block whose scale underflows to E4M3 zero encodes every element as a
     signed zero, whatever the element magnitudes are (tiny global scale)."""

@@ -108,6 +108,10 @@ def test_power_of_two_equivariance():
     assert P.check_pow2_equivariance(O.quantize_ref) == 0
 
 
+def test_requantising_the_dequantised_tensor_is_idempotent():
+    assert P.check_idempotence(O.quantize_ref, O.dequant_ref) == 0
+
+
 def test_sign_symmetry():
     assert P.check_sign_symmetry(O.quantize_ref) == 0
 

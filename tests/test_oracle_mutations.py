@@ -34,7 +34,7 @@ def _quant_pins(m):
             + P.check_dynamic_scale_maps_amax_to_top(m.quantize_ref) + P.check_sign_symmetry(m.quantize_ref)
             + P.check_e2m1_roundtrip(m.e2m1_decode, m.e2m1_encode) + P.check_e4m3_roundtrip(m.e4m3_decode, m.e4m3_encode)
             + P.check_e2m1_vs_fractions(m.e2m1_encode, n_random=2000) + P.check_e4m3_vs_fractions(m.e4m3_encode)
-            + P.check_underflowed_blocks_are_zero(m.quantize_ref))
+            + P.check_underflowed_blocks_are_zero(m.quantize_ref) + P.check_idempotence(m.quantize_ref, m.dequant_ref))
 
 
 QUANT_MUTANTS = {
