@@ -208,7 +208,8 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_decode_kernel(int64_t M_al
   // and a shift: exact for chunk < 2^14 and chunks_per_row < 2^12
   const uint64_t row_mag = (0xFFFFFFFFull + (uint64_t)chunks_per_row) / (uint64_t)chunks_per_row;
   auto chunk_row = [&](int f) { return (int)(((uint64_t)(uint32_t)f * row_mag) >> 32); };
-  constexpr int kChunksPer = kScaleLdsBytes / 16 / kThreads;  // the host guarantees n_chunks fits
+  // chunks per thread: enough for every chunk the host lets through (n_chunks * 16 <= kScaleLdsBytes)
+  constexpr int kChunksPer = (kScaleLdsBytes / 16 + kThreads - 1) / kThreads;
 
   auto load = [&](Super<MT, T>& b, int g) {
     g = max(0, min(g, G - 1));
@@ -639,33 +640,47 @@ bool gemm_decode_supported(int64_t m, int64_t n, int64_t k, const uint8_t* a_cod
 hipError_t launch_gemm_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                               const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
                               const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream) {
-  // up to 32 activation rows: the activations resident in LDS when they fit
-  // (K up to about 5.9K), with 16-byte staging loads, and when one workgroup
-  // per CU covers N in a single round (a second, partial round would cost
-  // more than the kernel saves)
-  const bool al_ok = (reinterpret_cast<uintptr_t>(a_codes) % 16) == 0 &&
-                     (reinterpret_cast<uintptr_t>(a_scales) % 16) == 0 &&
-                     (reinterpret_cast<uintptr_t>(w_scales) % 16) == 0 && m <= 32 &&
-                     (n + kAlRowsPerWg - 1) / kAlRowsPerWg <= device_cu_count();
-#define NVFP4_AL(MT)                                                                                           \
-  if (al_lds_bytes<MT, kAlT, kAlQ>(k) <= kAlLdsBytes)                                                          \
-    return launch_decode_al<MT, kAlT, kAlQ, kAlD>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales,   \
-                                                  w_gscale, c, out_dtype, ldc, stream);
-  if (al_ok && m <= 16) {
-    NVFP4_AL(1)
-  }
-  if (al_ok) {
-    NVFP4_AL(2)
-  }
-#undef NVFP4_AL
-  if (m <= 16)
-    return launch_decode_cfg<1, 4, 3>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype,
-                                      ldc, stream);
-  if (m <= 32)
+  // Up to 32 activation rows.  The time of a decode-shaped call is set by how
+  // many weight rows each CU streams and by the serial chain of each wave's
+  // super-groups, so the kernel is chosen by how many workgroups the shape
+  // gives against the chip's slots (3 per CU for the first kernel):
+  //  * 2 weight tiles per workgroup when that fits one round of slots;
+  //  * else the activations resident in LDS (one workgroup of 144 rows per
+  //    CU) when it fits, its grid fills one round and the operands are
+  //    16-byte aligned;
+  //  * else 3 weight tiles per workgroup (4 for up to 16 rows).
+  if (m <= 32) {
+    const int64_t cus = device_cu_count();
+    if ((n + 31) / 32 <= 3 * cus) {
+      if (m <= 16)
+        return launch_decode_cfg<1, 2, 3>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c,
+                                          out_dtype, ldc, stream);
+      return launch_decode_cfg<2, 2, 3>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c,
+                                        out_dtype, ldc, stream);
+    }
+    const bool al_ok = (reinterpret_cast<uintptr_t>(a_codes) % 16) == 0 &&
+                       (reinterpret_cast<uintptr_t>(a_scales) % 16) == 0 &&
+                       (reinterpret_cast<uintptr_t>(w_scales) % 16) == 0 &&
+                       (n + kAlRowsPerWg - 1) / kAlRowsPerWg <= cus;
+    if (m <= 16) {
+      if (al_ok && al_lds_bytes<1, kAlT, kAlQ>(k) <= kAlLdsBytes)
+        return launch_decode_al<1, kAlT, kAlQ, kAlD>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales,
+                                                     w_gscale, c, out_dtype, ldc, stream);
+      return launch_decode_cfg<1, 4, 3>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c,
+                                        out_dtype, ldc, stream);
+    }
+    if (al_ok && al_lds_bytes<2, kAlT, kAlQ>(k) <= kAlLdsBytes)
+      return launch_decode_al<2, kAlT, kAlQ, kAlD>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale,
+                                                   c, out_dtype, ldc, stream);
     return launch_decode_cfg<2, 3, 3>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype,
                                       ldc, stream);
+  }
   // 64 activation rows: one workgroup reads each weight line once for all of
-  // them; 2 waves per SIMD, since 3 would spill
+  // them, at 2 waves per SIMD (3 would spill); 2 weight tiles per workgroup
+  // when that fits one round of slots (2 per CU), else 3
+  if ((n + 31) / 32 <= 2 * (int64_t)device_cu_count())
+    return launch_decode_cfg<4, 2, 2>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype,
+                                      ldc, stream);
   return launch_decode_cfg<4, 3, 2>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype,
                                     ldc, stream);
 }
