@@ -70,9 +70,11 @@ struct DirectLoader {
   __amdgpu_buffer_rsrc_t codes_rsrc, scales_rsrc;
   uint32_t code_off[kCodeInstr];
   uint32_t scale_off[kScaleInstr];
+  int nk;  // stages of K
 
   __device__ __forceinline__ void init(const uint8_t* codes, const uint8_t* scales, int64_t row0, int64_t rows,
                                        int64_t k, int wave, int lane) {
+    nk = (int)(k / kBK);
     codes_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)codes, (short)0, (int)(rows * (k / 2)), 0x00020000);
     scales_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)scales, (short)0, (int)(rows * (k / 16)), 0x00020000);
 #pragma unroll
@@ -99,9 +101,18 @@ struct DirectLoader {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(codes_rsrc, (lds_void_t)(lds_codes + (wave * kCodeInstr + i) * 1024), 16,
                                              code_off[i], kt * kRowBytes, 0, 0);
   }
+  // A stage past the end of K (the loop runs whole groups of four stages)
+  // gets zero block scales instead, so every operand it decodes is zero; its
+  // code bytes are loaded as usual and multiplied by those zeros.
+  template <bool TAIL = true>
   __device__ __forceinline__ void issue_scale(lds_ptr_t lds_scales, int i, int kt, int wave) const {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(scales_rsrc, (lds_void_t)(lds_scales + (wave * kScaleInstr + i) * 256),
-                                             4, scale_off[i], kt * kBlocksPerStage, 0, 0);
+    const lds_ptr_t dst = lds_scales + (wave * kScaleInstr + i) * 256;
+    if (!TAIL || kt < nk) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(scales_rsrc, (lds_void_t)dst, 4, scale_off[i], kt * kBlocksPerStage, 0,
+                                               0);
+    } else {
+      reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(dst)[__lane_id()] = 0u;
+    }
   }
 };
 
@@ -141,12 +152,13 @@ struct Tile {
   }
 
   // the g-th of the stage's global loads (interleaved issue)
+  template <bool TAIL>
   __device__ __forceinline__ void issue_one(lds_ptr_t b, int kt, int g) {
     constexpr int C = DirectLoader<BM>::kCodeInstr, S = DirectLoader<BM>::kScaleInstr;
     if (g < C) la.issue_code(b + L::a_codes, g, kt, wave);
-    else if (g < C + S) la.issue_scale(b + L::a_scales, g - C, kt, wave);
+    else if (g < C + S) la.template issue_scale<TAIL>(b + L::a_scales, g - C, kt, wave);
     else if (g < 2 * C + S) lw.issue_code(b + L::w_codes, g - C - S, kt, wave);
-    else lw.issue_scale(b + L::w_scales, g - 2 * C - S, kt, wave);
+    else lw.template issue_scale<TAIL>(b + L::w_scales, g - 2 * C - S, kt, wave);
   }
 
   // LDS reads of fragment f (0..3 = A, 4..7 = W) of the stage held in buffer `st`
@@ -213,7 +225,7 @@ struct Tile {
   // (step 0 of `nxt` when S == 7).  Steps 0-5 also issue two of the twelve
   // global loads of stage kt+3 (slots 5 and 13); steps 2-5, after the barrier,
   // read two of the next stage's fragments from LDS (slots 0 and 8).
-  template <int S>
+  template <int S, bool TAIL>
   __device__ __forceinline__ void step_s(const Frags& cur, Frags& nxt, const uint8_t* rd, lds_ptr_t ld, int kt_load) {
 #pragma unroll
     for (int q = 0; q < FM * FN; ++q) {
@@ -229,7 +241,7 @@ struct Tile {
         if ((q & 7) == 0) read_frag(nxt, rd, 2 * (S - 2) + (q >> 3));
       }
       if constexpr (S <= 5) {
-        if ((q & 7) == 5) issue_one(ld, kt_load, 2 * S + (q >> 3));
+        if ((q & 7) == 5) issue_one<TAIL>(ld, kt_load, 2 * S + (q >> 3));
       }
       fence();
     }
@@ -240,19 +252,27 @@ struct Tile {
   // and `ld` (the buffer of stage kt-1, whose fragments every wave read during
   // stage kt-2) takes the global loads of stage kt+3.  Loads and reads issued
   // for stages past the end of K fetch data that is never multiplied.
+  // TAIL: some stage this one loads or waits for may lie past the end of K
+  // (only in the last iterations of the loop); it then checks.
+  template <bool TAIL>
   __device__ __forceinline__ void stage(int kt, const Frags& cur, Frags& nxt, const uint8_t* rd, lds_ptr_t ld) {
-    step_s<0>(cur, nxt, rd, ld, kt + 3);
-    step_s<1>(cur, nxt, rd, ld, kt + 3);
+    step_s<0, TAIL>(cur, nxt, rd, ld, kt + 3);
+    step_s<1, TAIL>(cur, nxt, rd, ld, kt + 3);
     // stage kt+1 landed once at most stage kt+2's twelve loads and the four
-    // of stage kt+3 issued in steps 0-1 are outstanding
-    wait_vmcnt<kLoadsPerStage + 4>();
+    // of stage kt+3 issued in steps 0-1 are outstanding; a stage past the end
+    // of K issues fewer loads (no scale loads), so near the end wait for all
+    if (TAIL && kt + 2 >= la.nk) {
+      wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<kLoadsPerStage + 4>();
+    }
     lds_barrier();
-    step_s<2>(cur, nxt, rd, ld, kt + 3);
-    step_s<3>(cur, nxt, rd, ld, kt + 3);
-    step_s<4>(cur, nxt, rd, ld, kt + 3);
-    step_s<5>(cur, nxt, rd, ld, kt + 3);
-    step_s<6>(cur, nxt, rd, ld, kt + 3);
-    step_s<7>(cur, nxt, rd, ld, kt + 3);
+    step_s<2, TAIL>(cur, nxt, rd, ld, kt + 3);
+    step_s<3, TAIL>(cur, nxt, rd, ld, kt + 3);
+    step_s<4, TAIL>(cur, nxt, rd, ld, kt + 3);
+    step_s<5, TAIL>(cur, nxt, rd, ld, kt + 3);
+    step_s<6, TAIL>(cur, nxt, rd, ld, kt + 3);
+    step_s<7, TAIL>(cur, nxt, rd, ld, kt + 3);
   }
 };
 
@@ -331,7 +351,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64
   t.issue_all(l0, 0);
   t.issue_all(l1, 1);
   t.issue_all(l2, 2);
-  wait_vmcnt<2 * kLoadsPerStage>();  // stage 0 landed
+  // stage 0 landed (a stage past the end of K issues no scale loads: wait for all then)
+  if (nk < 3) {
+    wait_vmcnt<0>();
+  } else {
+    wait_vmcnt<2 * kLoadsPerStage>();
+  }
   __syncthreads();
 
   Frags fx, fy;  // the two fragment register sets, used in turn
@@ -343,15 +368,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64
     if (q < 15) t.finish(0, q);  // chunk 15 is finished in the first slot of stage 0
   }
 
-  // Four stages per iteration (nk % 4 == 0): two register sets x four LDS
-  // buffers, all static.  Stage kt reads stage kt+1 from buffer (kt+1)%4 and
+  // Four stages per iteration (stages past nk, up to the next multiple of
+  // four, multiply zeros): two register sets x four LDS buffers, all static.  Stage kt reads stage kt+1 from buffer (kt+1)%4 and
   // loads stage kt+3 into buffer (kt+3)%4, which held stage kt-1 (already in
   // every wave's registers by the barrier of stage kt).
-  for (int kt = 0; kt < nk; kt += 4) {
-    t.stage(kt + 0, fx, fy, buf1, l3);
-    t.stage(kt + 1, fy, fx, buf2, l0);
-    t.stage(kt + 2, fx, fy, buf3, l1);
-    t.stage(kt + 3, fy, fx, buf0, l2);
+  // Iterations whose loads (stages kt+3 .. kt+6) all lie inside K take no
+  // checks, and so does every iteration when K is a whole number of groups
+  // of four stages (then no stage past the end is multiplied); otherwise the
+  // last one or two check every load and wait.
+  const int kt_plain = (nk & 3) == 0 ? nk : nk - 6;
+  int kt = 0;
+  for (; kt < kt_plain; kt += 4) {
+    t.stage<false>(kt + 0, fx, fy, buf1, l3);
+    t.stage<false>(kt + 1, fy, fx, buf2, l0);
+    t.stage<false>(kt + 2, fx, fy, buf3, l1);
+    t.stage<false>(kt + 3, fy, fx, buf0, l2);
+  }
+  for (; kt < nk; kt += 4) {
+    t.stage<true>(kt + 0, fx, fy, buf1, l3);
+    t.stage<true>(kt + 1, fy, fx, buf2, l0);
+    t.stage<true>(kt + 2, fx, fy, buf3, l1);
+    t.stage<true>(kt + 3, fy, fx, buf0, l2);
   }
   wait_vmcnt<0>();  // loads issued for stages past the end
 
@@ -447,7 +484,7 @@ bool gemm_fast_supported(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes
                        (reinterpret_cast<uintptr_t>(w_scales) % 4) == 0;
   // buffer offsets are 32-bit: each operand's code bytes must stay below 2^31
   const bool fits = m * (k / 2) < ((int64_t)1 << 31) && n * (k / 2) < ((int64_t)1 << 31);
-  return aligned && fits && k % (4 * kBK) == 0 && m > 64;  // stages in groups of four
+  return aligned && fits && k % kBK == 0 && m > 64;
 }
 
 hipError_t launch_gemm_fast(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
