@@ -38,8 +38,11 @@
 //  * Up to 32 activation rows with K up to about 5.9K, a second kernel keeps
 //    all activation codes and scale rows in LDS: a workgroup of three such
 //    quads of waves (one per CU) stages them once, and its main loop issues
-//    weight loads only.  Larger M or K, or operands off a 16-byte boundary,
-//    take the first kernel (64 rows at most).
+//    weight loads only.  The dispatch (launch_gemm_decode) picks between the
+//    two, and the weight rows per workgroup, by how many workgroups the
+//    shape gives against the chip's slots.
+//  * K % 256 == 128 (e.g. a row-parallel shard) ends in half a super-group:
+//    the first kernel zeroes the scales of its blocks past K.
 #include "gemm_common.h"
 #include "nvfp4_internal.h"
 
@@ -133,7 +136,7 @@ __device__ __forceinline__ void store_run4(void* c, int64_t ldc, int64_t m, int6
 // workgroup, OCC waves per SIMD.  SL: the workgroup's scale rows (weight and
 // activation, all of K) are staged in LDS once, with coalesced 16-byte loads,
 // instead of 4 bytes per row and super-group from memory.
-template <int MT, int T, int OCC, bool SL, int OUT>
+template <int MT, int T, int OCC, bool SL, bool KT, int OUT>
 __global__ __launch_bounds__(kThreads, OCC) void gemm_decode_kernel(int64_t M_all, int64_t N, int64_t K,
                                                                   const uint8_t* __restrict__ a_codes,
                                                                   const uint8_t* __restrict__ a_scales,
@@ -194,7 +197,8 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_decode_kernel(int64_t M_al
   }
 
   // this wave's super-groups
-  const int G = (int)(K / kSuperK);
+  // KT: K % 256 == 128, the last super-group holds only its first 128 elements
+  const int G = (int)((K + kSuperK - 1) / kSuperK);
   // super-groups wv, wv+4, wv+8, ...: the four waves read adjacent lines of
   // the same rows at about the same time (DRAM page locality)
   const int ng = (G - wv + kWaves - 1) / kWaves;
@@ -211,20 +215,25 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_decode_kernel(int64_t M_al
   // chunks per thread: enough for every chunk the host lets through (n_chunks * 16 <= kScaleLdsBytes)
   constexpr int kChunksPer = (kScaleLdsBytes / 16 + kThreads - 1) / kThreads;
 
+  // KT: in the last, half super-group the lanes with q >= 2 (blocks 8..15,
+  // past the end of K) read the first half's bytes again, inside the row;
+  // compute() zeroes their scale words, so they add nothing
+  auto past_k = [&](int g) { return KT && g == G - 1 && q >= 2; };
   auto load = [&](Super<MT, T>& b, int g) {
     g = max(0, min(g, G - 1));
     const int cs = g * (kSuperK / 2), ss = g * (kSuperK / 16);
+    const uint32_t back_c = past_k(g) ? 64u : 0u, back_s = past_k(g) ? 8u : 0u;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      b.w[t].c[0] = load16(wc_r, wc_off[t], cs);
-      b.w[t].c[1] = load16(wc_r, wc_off[t], cs + 16);
-      if constexpr (!SL) b.w[t].s = load4(ws_r, ws_off[t], ss);
+      b.w[t].c[0] = load16(wc_r, wc_off[t] - back_c, cs);
+      b.w[t].c[1] = load16(wc_r, wc_off[t] - back_c, cs + 16);
+      if constexpr (!SL) b.w[t].s = load4(ws_r, ws_off[t] - back_s, ss);
     }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      b.a[i].c[0] = load16(ac_r, ac_off[i], cs);
-      b.a[i].c[1] = load16(ac_r, ac_off[i], cs + 16);
-      if constexpr (!SL) b.a[i].s = load4(as_r, as_off[i], ss);
+      b.a[i].c[0] = load16(ac_r, ac_off[i] - back_c, cs);
+      b.a[i].c[1] = load16(ac_r, ac_off[i] - back_c, cs + 16);
+      if constexpr (!SL) b.a[i].s = load4(as_r, as_off[i] - back_s, ss);
     }
     // each super-group's loads stay together and in issue order (prologue and
     // loop alike), so the wait before its use counts only the one issued after it
@@ -238,6 +247,14 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_decode_kernel(int64_t M_al
     for (int t = 0; t < T; ++t) acc[i][t] = float4_v{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](Super<MT, T>& b, int g) {
+    if constexpr (KT) {
+      if (past_k(g)) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) b.w[t].s = 0u;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) b.a[i].s = 0u;
+      }
+    }
     if constexpr (SL) {
       // this lane's four scale bytes of super-group g (blocks 4q..4q+3)
       const int off = g * 16 + 4 * q;
@@ -604,20 +621,25 @@ hipError_t launch_decode_cfg(int64_t m, int64_t n, int64_t k, const uint8_t* a_c
   // staged scale rows: all of them must fit, and 16-byte loads need 16-byte aligned rows
   const bool sl = (int64_t)(16 * T + 16 * MT) * (k / 16) <= scale_lds_bytes<MT, T>() &&
                   (reinterpret_cast<uintptr_t>(a_scales) % 16) == 0 && (reinterpret_cast<uintptr_t>(w_scales) % 16) == 0;
-#define NVFP4_LAUNCH(SLV, OUT)                                                                                     \
-  gemm_decode_kernel<MT, T, OCC, SLV, OUT><<<grid, kThreads, 0, stream>>>(m, n, k, a_codes, a_scales, a_gscale, \
-                                                                         w_codes, w_scales, w_gscale, c, ldc)
-#define NVFP4_LAUNCH_OUT(SLV)   \
-  if (out_dtype == 0)           \
-    NVFP4_LAUNCH(SLV, 0);       \
-  else if (out_dtype == 1)      \
-    NVFP4_LAUNCH(SLV, 1);       \
-  else                          \
-    NVFP4_LAUNCH(SLV, 2);
-  if (sl) {
-    NVFP4_LAUNCH_OUT(true)
+#define NVFP4_LAUNCH(SLV, KTV, OUT)                                                                            \
+  gemm_decode_kernel<MT, T, OCC, SLV, KTV, OUT><<<grid, kThreads, 0, stream>>>(m, n, k, a_codes, a_scales,      \
+                                                                              a_gscale, w_codes, w_scales,     \
+                                                                              w_gscale, c, ldc)
+#define NVFP4_LAUNCH_OUT(SLV, KTV)   \
+  if (out_dtype == 0)                \
+    NVFP4_LAUNCH(SLV, KTV, 0);       \
+  else if (out_dtype == 1)           \
+    NVFP4_LAUNCH(SLV, KTV, 1);       \
+  else                               \
+    NVFP4_LAUNCH(SLV, KTV, 2);
+  // K % 256 == 128: a last half super-group, scales read from memory (the
+  // scale rows are then not whole 16-byte chunks for the LDS staging)
+  if (k % kSuperK != 0) {
+    NVFP4_LAUNCH_OUT(false, true)
+  } else if (sl) {
+    NVFP4_LAUNCH_OUT(true, false)
   } else {
-    NVFP4_LAUNCH_OUT(false)
+    NVFP4_LAUNCH_OUT(false, false)
   }
 #undef NVFP4_LAUNCH_OUT
 #undef NVFP4_LAUNCH
@@ -634,7 +656,7 @@ bool gemm_decode_supported(int64_t m, int64_t n, int64_t k, const uint8_t* a_cod
                        (reinterpret_cast<uintptr_t>(w_scales) % 4) == 0;
   // buffer offsets and sizes are 32-bit
   const bool fits = n * (k / 2) < ((int64_t)1 << 31) && m * (k / 2) < ((int64_t)1 << 31);
-  return aligned && fits && m <= kDecodeMaxRows && k % kSuperK == 0;
+  return aligned && fits && m <= kDecodeMaxRows && k % (kSuperK / 2) == 0;
 }
 
 hipError_t launch_gemm_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
@@ -660,7 +682,7 @@ hipError_t launch_gemm_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_
     }
     const bool al_ok = (reinterpret_cast<uintptr_t>(a_codes) % 16) == 0 &&
                        (reinterpret_cast<uintptr_t>(a_scales) % 16) == 0 &&
-                       (reinterpret_cast<uintptr_t>(w_scales) % 16) == 0 &&
+                       (reinterpret_cast<uintptr_t>(w_scales) % 16) == 0 && k % kSuperK == 0 &&
                        (n + kAlRowsPerWg - 1) / kAlRowsPerWg <= cus;
     if (m <= 16) {
       if (al_ok && al_lds_bytes<1, kAlT, kAlQ>(k) <= kAlLdsBytes)
