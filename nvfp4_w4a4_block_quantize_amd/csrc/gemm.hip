@@ -286,13 +286,36 @@ hipError_t launch_cfg(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, c
 
 }  // namespace
 
+namespace {
+
+// Between 65 and 256 activation rows both the prefill and the decode-shaped
+// kernels apply.  Estimated times, from measurements of both on MI355X:
+//  * prefill: rounds of 256x256 tiles over the CUs, about 0.0205 us per K
+//    element of a tile (105 us at K = 5120), however few rows a tile holds;
+//  * decode-shaped: one pass per 64-row block of activations, each streaming
+//    the weight at about 4.1e6 weight elements per us, at least 10 us.
+// The prefill kernel wins once its tiles fill the chip; with few tiles (small
+// N, or a single 256-row tile row at large K) the decode-shaped passes do.
+bool decode_beats_prefill(int64_t m, int64_t n, int64_t k) {
+  const int64_t cus = device_cu_count();
+  const int64_t tiles = ((m + 255) / 256) * ((n + 255) / 256);
+  const double prefill_us = (double)((tiles + cus - 1) / cus) * 0.0205 * (double)k;
+  const double pass_us = (double)n * (double)k / 4.1e6;
+  const double decode_us = (double)((m + 63) / 64) * (pass_us > 10.0 ? pass_us : 10.0);
+  return decode_us < prefill_us;
+}
+
+}  // namespace
+
 hipError_t launch_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                        const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
                        const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream) {
-  if (gemm_decode_supported(m, n, k, a_codes, a_scales, w_codes, w_scales))
+  const bool decode = gemm_decode_supported(m, n, k, a_codes, a_scales, w_codes, w_scales);
+  const bool prefill = gemm_fast_supported(m, n, k, a_codes, a_scales, w_codes, w_scales);
+  if (decode && (m <= 64 || !prefill || decode_beats_prefill(m, n, k)))
     return launch_gemm_decode(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype, ldc,
                               stream);
-  if (gemm_fast_supported(m, n, k, a_codes, a_scales, w_codes, w_scales))
+  if (prefill)
     return launch_gemm_fast(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype, ldc,
                             stream);
   const bool fast = (k % kBK) == 0 && (reinterpret_cast<uintptr_t>(a_codes) % 16) == 0 &&

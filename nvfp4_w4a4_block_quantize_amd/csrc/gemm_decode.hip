@@ -1,4 +1,5 @@
-// Decode-shaped W4A4 GEMM for gfx950 (M <= 64): C = alpha * A_hat W_hat^T on
+// Decode-shaped W4A4 GEMM for gfx950 (M <= 256, in blocks of up to 64 activation
+// rows): C = alpha * A_hat W_hat^T on
 // NVFP4 operands (news article "Qwen3.8-27B最激进4bit量化开源，权重显存暴降2.9倍！",
 // section 02: E2M1 codes, one E4M3 scale per 16 elements, one FP32 global
 // scale per tensor, both operands 4-bit).
@@ -59,7 +60,7 @@ template <int MT, int T>
 constexpr int scale_lds_bytes() {
   return kWaves * 16 * MT * (16 * T + 4) * 4 > 32768 ? kWaves * 16 * MT * (16 * T + 4) * 4 : 32768;
 }
-constexpr int64_t kDecodeMaxRows = 64;  // one 64-row block of activations at most
+constexpr int64_t kDecodeMaxRows = 256;  // up to four 64-row blocks of activations (grid.y)
 
 typedef float float4_v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -697,9 +698,11 @@ hipError_t launch_gemm_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_
     return launch_decode_cfg<2, 3, 3>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype,
                                       ldc, stream);
   }
-  // 64 activation rows: one workgroup reads each weight line once for all of
-  // them, at 2 waves per SIMD (3 would spill); 2 weight tiles per workgroup
-  // when that fits one round of slots (2 per CU), else 3
+  // 64 activation rows per workgroup (more in 64-row blocks along grid.y,
+  // which stream the same weight rows again, mostly from the caches): one
+  // workgroup reads each weight line once for all of them, at 2 waves per
+  // SIMD (3 would spill); 2 weight tiles per workgroup when a block's
+  // workgroups fit one round of slots (2 per CU), else 3
   if ((n + 31) / 32 <= 2 * (int64_t)device_cu_count())
     return launch_decode_cfg<4, 2, 2>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype,
                                       ldc, stream);

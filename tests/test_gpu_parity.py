@@ -173,8 +173,9 @@ def check_gemm(C, ref, bound, out_dtype):
     assert np.all(C[zero_rows] == 0)
 
 
-# m <= 64 or m > 64 with k % 128 == 0 take the decode-shaped (weight-streaming) and the main
-# prefill (direct-to-LDS) paths, everything else the generic one
+# with k % 128 == 0, m <= 64 takes the decode-shaped (weight-streaming) path, m > 256 the main
+# prefill (direct-to-LDS) path and 64 < m <= 256 whichever is estimated faster; other shapes the
+# generic one
 GEMM_SHAPES = [(64, 128, 256), (300, 520, 384), (1, 1, 16), (33, 257, 400), (256, 256, 128), (513, 300, 1056),
                (32, 1000, 640), (7, 333, 48), (64, 96, 4096),
                (16, 4352, 5120), (48, 777, 1024), (1, 300, 192), (32, 129, 64), (64, 33, 128), (32, 4096, 320),
@@ -187,6 +188,7 @@ GEMM_SHAPES = [(64, 128, 256), (300, 520, 384), (1, 1, 16), (33, 257, 400), (256
                (2048, 8256, 512),  # 264 tiles, a 64-column ragged edge at scale
                (100, 100, 128), (300, 1000, 640), (1024, 2000, 896), (520, 600, 2176), (2048, 1536, 2176),  # K % 512 != 0
                (32, 600, 2176), (9, 1000, 384), (64, 300, 640), (1, 130, 128), (20, 24577, 384), (48, 5000, 1152),  # K % 256 == 128
+               (96, 5000, 5120), (160, 4352, 2176), (250, 1024, 4096), (200, 700, 2176),  # 65-256 rows in 64-row decode blocks
                (65, 64, 256), (300, 520, 512), (513, 777, 1024), (257, 300, 256), (1000, 1000, 2560), (256, 512, 5120)]
 
 
