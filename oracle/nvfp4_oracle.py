@@ -304,16 +304,6 @@ def gemm_ref(a_codes, a_scales, g_a, w_codes, w_scales, g_w):
     return a @ w.T, np.abs(a) @ np.abs(w).T
 
 
-def gemm_ref_entries(a_codes, a_scales, g_a, w_codes, w_scales, g_w, rows, cols):
-    """C[rows[i], cols[i]] (and its |.| basis) one entry at a time, for spot
-    checks of shapes too large to multiply whole."""
-    rows = np.asarray(rows)
-    cols = np.asarray(cols)
-    a = dequant_ref(np.asarray(a_codes)[rows], np.asarray(a_scales)[rows], g_a)
-    w = dequant_ref(np.asarray(w_codes)[cols], np.asarray(w_scales)[cols], g_w)
-    return np.sum(a * w, axis=1), np.sum(np.abs(a * w), axis=1)
-
-
 # ---------------------------------------------------------------------------
 # Exact helpers for self-tests (rational arithmetic, no rounding at all)
 # ---------------------------------------------------------------------------
