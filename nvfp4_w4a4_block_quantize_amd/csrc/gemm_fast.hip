@@ -1,7 +1,7 @@
 // Main GEMM path for gfx950: C = alpha * A_hat W_hat^T on NVFP4 operands
 // (news article "Qwen3.8-27B最激进4bit量化开源，权重显存暴降2.9倍！", section 02:
 // the W4A4 product of E2M1 codes with E4M3 scales per 16 elements and an FP32
-// global scale per tensor), for k % 512 == 0.
+// global scale per tensor), for k % 128 == 0.
 //
 // Tile: 256 x 256 per workgroup of 4 waves (2 x 2), 128 x 128 per wave = 4 x 4
 // MFMA 32x32x16 tiles, 256 FP32 accumulators per lane.  One stage = 128 K

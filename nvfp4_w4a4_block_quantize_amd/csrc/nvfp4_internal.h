@@ -34,14 +34,15 @@ hipError_t launch_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, 
                        const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
                        const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream);
 
-// Main GEMM path (k % 128 == 0, m > 64, 16-byte aligned codes, operands below 2 GiB).
+// Main GEMM path (k % 128 == 0, m > 64, 16-byte aligned codes, 4-byte aligned scales, operands below 2 GiB).
 bool gemm_fast_supported(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                          const uint8_t* w_codes, const uint8_t* w_scales);
 hipError_t launch_gemm_fast(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                             const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
                             const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream);
 
-// Decode-shaped path (m <= 64, k % 64 == 0, 16-byte aligned codes, operands below 2 GiB).
+// Decode-shaped path (m <= 256 in blocks of 64 rows, k % 128 == 0, 16-byte aligned codes, 4-byte aligned
+// scales, operands below 2 GiB).
 bool gemm_decode_supported(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                            const uint8_t* w_codes, const uint8_t* w_scales);
 hipError_t launch_gemm_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
