@@ -371,6 +371,27 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_decode_kernel(int64_t M_al
 // fragments from LDS.  Q quads share one copy of A, so A is read from L2 Q
 // times less often as well.
 constexpr int kAlLdsBytes = 160 * 1024;  // all of a CU's LDS: one workgroup per CU
+__host__ __device__ constexpr int64_t kib_round(int64_t bytes) { return (bytes + 1023) / 1024 * 1024; }
+
+typedef __attribute__((address_space(3))) uint8_t* lds_ptr_t;
+typedef __attribute__((address_space(3))) void* lds_void_t;
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// s_waitcnt vmcnt(N), LDS and export counters unconstrained (the 6-bit vmcnt
+// field is split over bits 3:0 and 15:14)
+template <int N>
+__device__ __forceinline__ void al_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
+}
+// workgroup barrier ordering LDS only (direct-to-LDS loads are ordered by the
+// explicit vmcnt wait before it; the weight loads still in flight need not drain)
+__device__ __forceinline__ void al_lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+#endif
 constexpr int kAlPad = 16;  // bytes added to each staged row: rows r and r+1 start 4 banks apart
 constexpr int kAlT = 3, kAlQ = 3;  // 3 weight tiles per quad, 3 quads (12 waves) per workgroup
 constexpr int kAlD = 2;  // super-groups of weight loads in flight per wave
@@ -404,11 +425,15 @@ __global__ __launch_bounds__(kThreads * Q, Q) void gemm_decode_al_kernel(int64_t
   const int64_t code_ld = K / 2, scale_ld = K / 16;
   const int apitch = (int)code_ld + kAlPad;   // LDS bytes per activation code row
   const int spitch = (int)scale_ld + kAlPad;  // LDS bytes per scale row
-  // LDS: activation codes [kRows][apitch], then scale rows [Q*R weight rows,
-  // quad-major, then kRows activation rows][spitch]; after the main loop the
-  // quads' partial sums overwrite the front
+  // LDS: activation codes [kRows][apitch], weight scale rows [Q*R, quad-major]
+  // [spitch], activation scale rows [kRows][spitch], each region rounded up to
+  // whole KiB; after the main loop the quads' partial sums overwrite the front
+  const int a_bytes = (int)kib_round((int64_t)kRows * apitch);
+  const int sw_bytes = (int)kib_round((int64_t)(Q * R) * spitch);
+  const int sa_bytes = (int)kib_round((int64_t)kRows * spitch);
   uint8_t* const lds_a = lds;
-  uint8_t* const lds_s = lds + kRows * apitch;
+  uint8_t* const lds_sw = lds + a_bytes;
+  uint8_t* const lds_sa = lds_sw + sw_bytes;
 
   const __amdgpu_buffer_rsrc_t wc_r =
       __builtin_amdgcn_make_buffer_rsrc((void*)w_codes, (short)0, (int)(N * code_ld), 0x00020000);
@@ -455,11 +480,11 @@ __global__ __launch_bounds__(kThreads * Q, Q) void gemm_decode_al_kernel(int64_t
       const uint8_t* pa = lds_a + (16 * i + lr) * apitch + g * (kSuperK / 2) + 32 * q;
       a[i].c[0] = *reinterpret_cast<const uint4*>(pa);
       a[i].c[1] = *reinterpret_cast<const uint4*>(pa + 16);
-      a[i].s = *reinterpret_cast<const uint32_t*>(lds_s + (Q * R + 16 * i + lr) * spitch + g * 16 + 4 * q);
+      a[i].s = *reinterpret_cast<const uint32_t*>(lds_sa + (16 * i + lr) * spitch + g * 16 + 4 * q);
     }
 #pragma unroll
     for (int t = 0; t < T; ++t)
-      ws[t] = *reinterpret_cast<const uint32_t*>(lds_s + (qd * R + 16 * t + lr) * spitch + g * 16 + 4 * q);
+      ws[t] = *reinterpret_cast<const uint32_t*>(lds_sw + (qd * R + 16 * t + lr) * spitch + g * 16 + 4 * q);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       auto scale_of = [&](uint32_t w) {
@@ -480,72 +505,46 @@ __global__ __launch_bounds__(kThreads * Q, Q) void gemm_decode_al_kernel(int64_t
     }
   };
 
-  // Staging, in three segments of 16-byte chunks: activation code rows,
-  // weight scale rows, activation scale rows.  Chunk f of a segment is row
-  // f / cpr, chunk f % cpr (a multiply with ceil(2^32 / cpr): exact while
-  // f * cpr < 2^32); rows past M or N repeat the last row (never stored) and
-  // threads past the end repeat the segment's last chunk (same bytes to the
-  // same place).  One batch of loads covers all three segments for K up to
-  // 6144; every staging load goes out before the weight loads (loads
-  // complete in issue order: the staging data is not held behind HBM
-  // latency), and a chunk loop covers what a batch misses.
-  constexpr int TH = kThreads * Q;
-  constexpr int UA = 4 * MT, UW = (Q * R * 24 + TH - 1) / TH, US = (kRows * 24 + TH - 1) / TH;
-  const int cpr_a = (int)(code_ld / 16), cpr_s = (int)(scale_ld / 16);
-  const int n_a = kRows * cpr_a, n_w = Q * R * cpr_s, n_s = kRows * cpr_s;
-  // ceil(2^32 / cpr) = floor((2^32 - 1) / cpr) + 1, by a 32-bit division
-  const uint64_t mag_a = (uint64_t)(0xFFFFFFFFu / (uint32_t)cpr_a) + 1;
-  const uint64_t mag_s = (uint64_t)(0xFFFFFFFFu / (uint32_t)cpr_s) + 1;
-  auto row_of = [](int f, uint64_t mag) { return (int)(((uint64_t)(uint32_t)f * mag) >> 32); };
-  // segment chunk f -> source address and LDS offset
-  auto a_src = [&](int f) {
-    const int r = row_of(f, mag_a), ch = f - r * cpr_a;
-    return a_codes + min((int64_t)r, M - 1) * code_ld + 16 * ch;
+  // Staging, with direct-to-LDS buffer loads: one instruction moves 64 lanes
+  // x 16 bytes into 1 KiB of consecutive LDS, each lane fetching the global
+  // chunk that belongs at its slot.  No register holds a staged byte, so the
+  // weight loads of all D super-groups go out at the start, right behind the
+  // staging loads (a wave's loads complete in issue order).  Three regions,
+  // each a whole number of KiB: activation code rows (pitch apitch), weight
+  // scale rows and activation scale rows (pitch spitch).  Slot byte P of a
+  // region is row P / pitch (a multiply with ceil(2^32 / pitch), exact while
+  // P * pitch < 2^32) and column P % pitch; pad columns, rows past M or N and
+  // the rounding tail fetch bytes of an existing row, never read as data.
+  const lds_ptr_t lbase = (lds_ptr_t)lds;
+  auto stage_region = [&](lds_ptr_t dst, int bytes, __amdgpu_buffer_rsrc_t src, int pitch, int64_t row0,
+                          int64_t rows, int64_t ld) {
+    const uint64_t mag = (uint64_t)(0xFFFFFFFFu / (uint32_t)pitch) + 1;
+    for (int i = wave; i < bytes / 1024; i += kWaves * Q) {
+      const uint32_t pos = (uint32_t)(i * 1024 + lane * 16);
+      const uint32_t r = (uint32_t)(((uint64_t)pos * mag) >> 32);
+      const uint32_t col = pos - r * (uint32_t)pitch;
+      const int64_t gr = min(row0 + (int64_t)r, rows - 1);
+      const uint32_t off = (uint32_t)(gr * ld) + (col < (uint32_t)ld ? col : 0u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t)(dst + i * 1024), 16, off, 0, 0, 0);
+    }
   };
-  auto a_dst = [&](int f) {
-    const int r = row_of(f, mag_a);
-    return r * apitch + 16 * (f - r * cpr_a);
-  };
-  auto w_src = [&](int f) {
-    const int r = row_of(f, mag_s), ch = f - r * cpr_s;
-    return w_scales + min(wg_row0 + r, N - 1) * scale_ld + 16 * ch;
-  };
-  auto s_src = [&](int f) {
-    const int r = row_of(f, mag_s), ch = f - r * cpr_s;
-    return a_scales + min((int64_t)r, M - 1) * scale_ld + 16 * ch;
-  };
-  auto sc_dst = [&](int row0, int f) {  // scale segment starting at scale row row0
-    const int r = row_of(f, mag_s);
-    return kRows * apitch + (row0 + r) * spitch + 16 * (f - r * cpr_s);
-  };
-
+  stage_region(lbase, a_bytes,
+               __builtin_amdgcn_make_buffer_rsrc((void*)a_codes, (short)0, (int)(M * code_ld), 0x00020000), apitch, 0,
+               M, code_ld);
+  stage_region(lbase + a_bytes, sw_bytes,
+               __builtin_amdgcn_make_buffer_rsrc((void*)w_scales, (short)0, (int)(N * scale_ld), 0x00020000), spitch,
+               wg_row0, N, scale_ld);
+  stage_region(lbase + a_bytes + sw_bytes, sa_bytes,
+               __builtin_amdgcn_make_buffer_rsrc((void*)a_scales, (short)0, (int)(M * scale_ld), 0x00020000), spitch, 0,
+               M, scale_ld);
+  __builtin_amdgcn_sched_barrier(0);
   WCodes b[D][T];
-  {
-    u32x4_t va[UA], vw[UW], vs[US];
 #pragma unroll
-    for (int u = 0; u < UA; ++u) va[u] = *reinterpret_cast<const u32x4_t*>(a_src(min(u * TH + tid, n_a - 1)));
-#pragma unroll
-    for (int u = 0; u < UW; ++u) vw[u] = *reinterpret_cast<const u32x4_t*>(w_src(min(u * TH + tid, n_w - 1)));
-#pragma unroll
-    for (int u = 0; u < US; ++u) vs[u] = *reinterpret_cast<const u32x4_t*>(s_src(min(u * TH + tid, n_s - 1)));
-    load_w(b[0], gidx(0));
-#pragma unroll
-    for (int u = 0; u < UA; ++u) *reinterpret_cast<u32x4_t*>(lds + a_dst(min(u * TH + tid, n_a - 1))) = va[u];
-#pragma unroll
-    for (int u = 0; u < UW; ++u) *reinterpret_cast<u32x4_t*>(lds + sc_dst(0, min(u * TH + tid, n_w - 1))) = vw[u];
-#pragma unroll
-    for (int u = 0; u < US; ++u) *reinterpret_cast<u32x4_t*>(lds + sc_dst(Q * R, min(u * TH + tid, n_s - 1))) = vs[u];
-  }
-  for (int f = UA * TH + tid; f < n_a; f += TH)
-    *reinterpret_cast<u32x4_t*>(lds + a_dst(f)) = *reinterpret_cast<const u32x4_t*>(a_src(f));
-  for (int f = UW * TH + tid; f < n_w; f += TH)
-    *reinterpret_cast<u32x4_t*>(lds + sc_dst(0, f)) = *reinterpret_cast<const u32x4_t*>(w_src(f));
-  for (int f = US * TH + tid; f < n_s; f += TH)
-    *reinterpret_cast<u32x4_t*>(lds + sc_dst(Q * R, f)) = *reinterpret_cast<const u32x4_t*>(s_src(f));
-  // the other super-groups' weight loads once the staging registers are free
-#pragma unroll
-  for (int d = 1; d < D; ++d) load_w(b[d], gidx(min(d, max(ng - 1, 0))));
-  __syncthreads();
+  for (int d = 0; d < D; ++d) load_w(b[d], gidx(min(d, max(ng - 1, 0))));
+  // this wave's staging loads have landed once only its 2*T*D weight loads
+  // may be outstanding; then every wave's have, after the barrier
+  al_wait_vmcnt<2 * T * D>();
+  al_lds_barrier();
 
   // D super-groups of weight loads in flight per wave
   int j = 0;
@@ -591,7 +590,8 @@ __global__ __launch_bounds__(kThreads * Q, Q) void gemm_decode_al_kernel(int64_t
 // LDS bytes the kernel above stages for these sizes
 template <int MT, int T, int Q>
 constexpr int64_t al_lds_bytes(int64_t k) {
-  return (int64_t)(16 * MT) * (k / 2 + kAlPad) + (int64_t)(Q * 16 * T + 16 * MT) * (k / 16 + kAlPad);
+  return kib_round((int64_t)(16 * MT) * (k / 2 + kAlPad)) + kib_round((int64_t)(Q * 16 * T) * (k / 16 + kAlPad)) +
+         kib_round((int64_t)(16 * MT) * (k / 16 + kAlPad));
 }
 
 // D super-groups of weight loads in flight per wave

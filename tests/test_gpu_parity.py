@@ -183,6 +183,7 @@ GEMM_SHAPES = [(64, 128, 256), (300, 520, 384), (1, 1, 16), (33, 257, 400), (256
                (32, 520, 17408), (8, 2000, 5120), (32, 700, 6144),
                (64, 4352, 5120), (57, 300, 8192), (40, 130, 7424), (64, 70, 7680),  # 64-row decode block
                (9, 200, 9216), (5, 130, 17408), (24, 1100, 6144), (3, 9000, 4096), (12, 37000, 512),  # LDS-resident A or not
+               (32, 30000, 5888), (16, 25000, 5632),  # LDS-resident A near the size of the LDS
                (2, 1, 256), (32, 5, 512), (4, 36864, 256), (4, 36865, 256),  # fewer rows than a tile; one round or not
                (32, 30000, 512), (16, 26000, 1024), (20, 24576, 512), (20, 24577, 512), (40, 17000, 256),  # kernel choice by grid
                (2048, 8256, 512),  # 264 tiles, a 64-column ragged edge at scale
