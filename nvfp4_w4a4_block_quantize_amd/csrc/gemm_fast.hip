@@ -53,13 +53,20 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
-// Workgroup barrier ordering LDS only.  Direct-to-LDS loads are ordered by the
-// explicit vmcnt wait before it, so the still-outstanding loads of later stages
-// need not drain (a full __syncthreads() would wait for them).
+// Workgroup barrier for the stage buffers.  Each wave's direct-to-LDS loads of
+// the stage about to be read are complete once the explicit vmcnt wait before
+// the barrier returns (loads complete in issue order), so the loads of later
+// stages may stay in flight across it.  A workgroup-scope release fence on LDS
+// cannot be used here: direct-to-LDS loads count as LDS writes, so it waits
+// for every one in flight (vmcnt(0)), which would drain the prefetch at every
+// stage.  Instead the wave waits for its own LDS reads (lgkmcnt(0): no buffer
+// is refilled while a read of it is pending), and the wavefront-scope fences
+// only keep the compiler from moving LDS accesses across the barrier.
 __device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
   __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int ROWS>
@@ -357,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64
   } else {
     wait_vmcnt<2 * kLoadsPerStage>();
   }
-  __syncthreads();
+  lds_barrier();
 
   Frags fx, fy;  // the two fragment register sets, used in turn
 #pragma unroll
