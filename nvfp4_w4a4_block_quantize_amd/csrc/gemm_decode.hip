@@ -265,25 +265,39 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_decode_kernel(int64_t M_al
       for (int i = 0; i < MT; ++i)
         b.a[i].s = *reinterpret_cast<const uint32_t*>(lds + (R + 16 * i + lr) * srow + off);
     }
+    // scale byte s/2 of a lane's four, as an fp16 pair (exact), broadcast
+    auto scale_at = [&](uint32_t w, int s) {
+      const half2_t sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w >> (16 * (s >> 2)), 1.0f, false);
+      const _Float16 v = sp[(s >> 1) & 1];
+      return half2_t{v, v};
+    };
+    // software pipeline over the 8*T (step, weight tile) regions, one weight
+    // fragment per scheduling region: the MFMAs of region r are issued before
+    // the decode of region r+1 (the activation fragments are decoded with the
+    // first region of each step)
+    half8_t fa[MT], fw;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      // scale byte s/2 of a lane's four, as an fp16 pair (exact), broadcast
-      auto scale_of = [&](uint32_t w) {
-        const half2_t sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w >> (16 * (s >> 2)), 1.0f, false);
-        const _Float16 v = sp[(s >> 1) & 1];
-        return half2_t{v, v};
-      };
-      half8_t fa[MT];
+    for (int i = 0; i < MT; ++i) fa[i] = decode8(word_at(b.a[i].c, 0), scale_at(b.a[i].s, 0));
+    fw = decode8(word_at(b.w[0].c, 0), scale_at(b.w[0].s, 0));
 #pragma unroll
-      for (int i = 0; i < MT; ++i) fa[i] = decode8(word_at(b.a[i].c, s), scale_of(b.a[i].s));
+    for (int r = 0; r < 8 * T; ++r) {
+      const int t = r % T;
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const half8_t fw = decode8(word_at(b.w[t].c, s), scale_of(b.w[t].s));
+      for (int i = 0; i < MT; ++i) acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw, fa[i], acc[i][t], 0, 0, 0);
+      if (r + 1 < 8 * T) {
+        const int s2 = (r + 1) / T, t2 = (r + 1) % T;
+        const half8_t fw2 = decode8(word_at(b.w[t2].c, s2), scale_at(b.w[t2].s, s2));
+        half8_t fa2[MT];
+        if (t2 == 0) {
 #pragma unroll
-        for (int i = 0; i < MT; ++i) acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw, fa[i], acc[i][t], 0, 0, 0);
-        // one weight fragment per scheduling region: decoding a whole step (or
-        // several) up front would run out of registers at three waves per SIMD
+          for (int i = 0; i < MT; ++i) fa2[i] = decode8(word_at(b.a[i].c, s2), scale_at(b.a[i].s, s2));
+        }
         __builtin_amdgcn_sched_barrier(0);
+        fw = fw2;
+        if (t2 == 0) {
+#pragma unroll
+          for (int i = 0; i < MT; ++i) fa[i] = fa2[i];
+        }
       }
     }
   };
@@ -485,22 +499,36 @@ __global__ __launch_bounds__(kThreads * Q, Q) void gemm_decode_al_kernel(int64_t
 #pragma unroll
     for (int t = 0; t < T; ++t)
       ws[t] = *reinterpret_cast<const uint32_t*>(lds_sw + (qd * R + 16 * t + lr) * spitch + g * 16 + 4 * q);
+    auto scale_at = [&](uint32_t w, int s) {
+      const half2_t sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w >> (16 * (s >> 2)), 1.0f, false);
+      const _Float16 v = sp[(s >> 1) & 1];
+      return half2_t{v, v};
+    };
+    // software pipeline over the 8*T (step, weight tile) regions: the MFMAs of
+    // region r are issued before the decode of region r+1
+    half8_t fa[MT], fw;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      auto scale_of = [&](uint32_t w) {
-        const half2_t sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w >> (16 * (s >> 2)), 1.0f, false);
-        const _Float16 v = sp[(s >> 1) & 1];
-        return half2_t{v, v};
-      };
-      half8_t fa[MT];
+    for (int i = 0; i < MT; ++i) fa[i] = decode8(word_at(a[i].c, 0), scale_at(a[i].s, 0));
+    fw = decode8(word_at(bw[0].c, 0), scale_at(ws[0], 0));
 #pragma unroll
-      for (int i = 0; i < MT; ++i) fa[i] = decode8(word_at(a[i].c, s), scale_of(a[i].s));
+    for (int r = 0; r < 8 * T; ++r) {
+      const int t = r % T;
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const half8_t fw = decode8(word_at(bw[t].c, s), scale_of(ws[t]));
+      for (int i = 0; i < MT; ++i) acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw, fa[i], acc[i][t], 0, 0, 0);
+      if (r + 1 < 8 * T) {
+        const int s2 = (r + 1) / T, t2 = (r + 1) % T;
+        const half8_t fw2 = decode8(word_at(bw[t2].c, s2), scale_at(ws[t2], s2));
+        half8_t fa2[MT];
+        if (t2 == 0) {
 #pragma unroll
-        for (int i = 0; i < MT; ++i) acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fw, fa[i], acc[i][t], 0, 0, 0);
+          for (int i = 0; i < MT; ++i) fa2[i] = decode8(word_at(a[i].c, s2), scale_at(a[i].s, s2));
+        }
         __builtin_amdgcn_sched_barrier(0);
+        fw = fw2;
+        if (t2 == 0) {
+#pragma unroll
+          for (int i = 0; i < MT; ++i) fa[i] = fa2[i];
+        }
       }
     }
   };
