@@ -11,6 +11,10 @@
 //     exact value (bias 7, subnormals m * 2^-9).
 //  4. v_cvt_pk_bf16_f32 (GEMM epilogue, bf16 output): fp32 to bf16 nearest,
 //     ties to even, compared for every non-NaN fp32 bit pattern.
+//  5. v_cvt_pk_fp8_f32 after a clamp to [-448, 448] (FP8 KV quantiser):
+//     E4M3FN nearest, ties to even, saturating at 448, sign bit copied from
+//     y, in all four byte positions; compared for every non-NaN fp32 bit
+//     pattern.
 //
 // Prints one line per check and exits 0 only when every count of mismatches
 // is zero.  Built next to the library; run by the GPU test suite.
@@ -74,6 +78,52 @@ __global__ void check_bf16_pack(unsigned long long* bad) {
   if (nb) atomicAdd(bad, nb);
 }
 
+// E4M3FN of y: |y| clamped to 448, then nearest, ties to even, on the grid
+// m * 2^-9 (m = 0..8) below 2^-6 and (1 + f/8) * 2^(e-7) above; sign from y
+__device__ uint32_t e4m3_rule(float y) {
+  const float a = fminf(__builtin_fabsf(y), 448.0f);
+  uint32_t mag;
+  if (a < 0x1p-6f) {
+    mag = (uint32_t)rintf(a * 512.0f);  // 8 is the smallest normal, 0x08
+  } else {
+    int e;
+    const float m = frexpf(a, &e);  // a = m * 2^e, m in [0.5, 1)
+    uint32_t q = (uint32_t)rintf(m * 16.0f);  // 8..16: the significand with three fraction bits
+    if (q == 16u) {
+      q = 8u;
+      ++e;
+    }
+    mag = ((uint32_t)(e + 6) << 3) | (q - 8u);  // biased exponent (e - 1) + 7
+  }
+  return mag | ((__float_as_uint(y) >> 24) & 0x80u);
+}
+
+__device__ float clamp448(float y) { return __builtin_amdgcn_fmed3f(y, -448.0f, 448.0f); }
+
+__global__ void check_fp8_encode(unsigned long long* bad) {
+  unsigned long long nb = 0;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 32); i += 2 * stride) {
+    const uint32_t u0 = (uint32_t)i;
+    const uint32_t u1 = (uint32_t)(i + stride);  // i + stride < 2^32: i < 2^32 - 2*stride at every step
+    const float y0 = __uint_as_float(u0), y1 = __uint_as_float(u1);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(y0), clamp448(y1), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(y1), clamp448(y0), w, true);
+    const uint32_t hw = (uint32_t)w;
+    if ((u0 & 0x7FFFFFFFu) <= 0x7F800000u) {
+      const uint32_t r = e4m3_rule(y0);
+      nb += (hw & 0xFFu) != r;
+      nb += ((hw >> 24) & 0xFFu) != r;
+    }
+    if ((u1 & 0x7FFFFFFFu) <= 0x7F800000u) {
+      const uint32_t r = e4m3_rule(y1);
+      nb += ((hw >> 8) & 0xFFu) != r;
+      nb += ((hw >> 16) & 0xFFu) != r;
+    }
+  }
+  if (nb) atomicAdd(bad, nb);
+}
+
 __global__ void check_decodes(unsigned long long* bad) {
   const uint32_t t = threadIdx.x;  // 0..255
   unsigned long long nb = 0;
@@ -93,17 +143,19 @@ __global__ void check_decodes(unsigned long long* bad) {
 
 int main() {
   unsigned long long* bad = nullptr;
-  if (hipMalloc(&bad, 3 * sizeof(unsigned long long)) != hipSuccess) return 2;
-  if (hipMemset(bad, 0, 3 * sizeof(unsigned long long)) != hipSuccess) return 2;
+  if (hipMalloc(&bad, 4 * sizeof(unsigned long long)) != hipSuccess) return 2;
+  if (hipMemset(bad, 0, 4 * sizeof(unsigned long long)) != hipSuccess) return 2;
   check_fp4_encode<<<4096, 256>>>(bad);
   check_decodes<<<1, 256>>>(bad + 1);
   check_bf16_pack<<<4096, 256>>>(bad + 2);
-  unsigned long long h[3] = {1, 1, 1};
+  check_fp8_encode<<<4096, 256>>>(bad + 3);
+  unsigned long long h[4] = {1, 1, 1, 1};
   if (hipDeviceSynchronize() != hipSuccess) return 2;
   if (hipMemcpy(h, bad, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return 2;
   printf("fp4 encode (all non-NaN fp32 inputs): %llu mismatches\n", h[0]);
   printf("fp4->f16, e4m3->f16, e4m3->f32 decodes (all codes): %llu mismatches\n", h[1]);
   printf("fp32->bf16 pack (all non-NaN fp32 inputs): %llu mismatches\n", h[2]);
+  printf("clamped fp32->e4m3 pack (all non-NaN fp32 inputs): %llu mismatches\n", h[3]);
   hipFree(bad);
-  return (h[0] == 0 && h[1] == 0 && h[2] == 0) ? 0 : 1;
+  return (h[0] == 0 && h[1] == 0 && h[2] == 0 && h[3] == 0) ? 0 : 1;
 }

@@ -6,9 +6,12 @@
 //
 // Every element becomes q = sign(y) | E4M3FN_nearest_even_saturating(|y|) with
 // y = fp32(x * s); s is the ENCODE scale (448 / calibrated amax), read from
-// device memory, and the dequantised value is e4m3(q) / s.  Bandwidth kernel:
-// 2 B read + 1 B written per bf16 element; one lane owns 8 elements (16 B
-// in, 8 B out), four such chunks in flight per thread.
+// device memory, and the dequantised value is e4m3(q) / s.  The encode is
+// v_cvt_pk_fp8_f32 on y clamped to [-448, 448] (two elements per
+// instruction); that pair equals the rule above on every non-NaN fp32 input
+// (checked exhaustively by conformance_cvt).  Bandwidth kernel: 2 B read +
+// 1 B written per bf16 element; one lane owns 8 elements (16 B in, 8 B out),
+// four such chunks in flight per thread.
 #include "nvfp4_device.h"
 #include "nvfp4_internal.h"
 
@@ -49,8 +52,11 @@ __device__ __forceinline__ void load8(const void* x, int64_t elem, float (&f)[8]
   }
 }
 
-__device__ __forceinline__ uint32_t e4m3_signed(float y) {
-  return e4m3_from_f32(__builtin_fabsf(y)) | ((__float_as_uint(y) >> 24) & 0x80u);
+// four E4M3 bytes of y[0..3], y[0] in the low byte
+__device__ __forceinline__ uint32_t e4m3x4(float y0, float y1, float y2, float y3) {
+  auto clamp = [](float y) { return __builtin_amdgcn_fmed3f(y, -448.0f, 448.0f); };
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(clamp(y0), clamp(y1), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp(y2), clamp(y3), lo, true);
 }
 
 template <int DT, bool DENSE>
@@ -77,9 +83,8 @@ __global__ __launch_bounds__(kThreads) void kv_quantize_kernel(const void* __res
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int64_t c = base + u * kThreads;
-    u32x2_t w = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[i >> 2] |= e4m3_signed(f[u][i] * s) << (8 * (i & 3));
+    const u32x2_t w = {e4m3x4(f[u][0] * s, f[u][1] * s, f[u][2] * s, f[u][3] * s),
+                       e4m3x4(f[u][4] * s, f[u][5] * s, f[u][6] * s, f[u][7] * s)};
     if (c < total_chunks) out[c] = w;
   }
 }
