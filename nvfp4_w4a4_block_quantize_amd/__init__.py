@@ -89,18 +89,30 @@ def _torch():
     return torch
 
 
+_DTYPES = {}
+
+
 def _dtype_code(dtype) -> int:
-    torch = _torch()
-    table = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
-    if dtype not in table:
+    if not _DTYPES:
+        torch = _torch()
+        _DTYPES.update({torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16})
+    if dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {dtype}")
-    return table[dtype]
+    return _DTYPES[dtype]
 
 
-def _stream_ptr(stream=None) -> int:
+def _stream_ptr(stream=None, like=None) -> int:
+    """hipStream_t of `stream`, else torch's current stream on the device of
+    tensor `like` (or the current device).  torch's raw-stream accessor skips
+    building a Stream object, which costs more than the rest of a call."""
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return int(s.cuda_stream)
+    if stream is not None:
+        return int(stream.cuda_stream)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    index = like.get_device() if like is not None else torch.cuda.current_device()
+    if raw is not None:
+        return int(raw(index))
+    return int(torch.cuda.current_stream(index).cuda_stream)
 
 
 def _dev(t, name):
@@ -127,7 +139,7 @@ def nvfp4_quantize(x, gscale, mode: str = "static", codes=None, scales=None, str
     m = {"static": GSCALE_STATIC, "dynamic": GSCALE_DYNAMIC}[mode]
     st = load_library().nvfp4_quantize(_dev(x, "x"), _dtype_code(x.dtype), rows, cols, x.stride(0),
                                        _dev(gscale, "gscale"), m, _dev(codes, "codes"), _dev(scales, "scales"),
-                                       _stream_ptr(stream))
+                                       _stream_ptr(stream, x))
     _check("nvfp4_quantize", st)
     return codes, scales
 
@@ -139,7 +151,7 @@ def nvfp4_amax_observe(x, amax_state, stream=None):
         raise ValueError("x must be 2-D with unit column stride")
     rows, cols = x.shape
     st = load_library().nvfp4_amax_observe(_dev(x, "x"), _dtype_code(x.dtype), rows, cols, x.stride(0),
-                                           _dev(amax_state, "amax_state"), _stream_ptr(stream))
+                                           _dev(amax_state, "amax_state"), _stream_ptr(stream, x))
     _check("nvfp4_amax_observe", st)
     return amax_state
 
@@ -150,7 +162,7 @@ def nvfp4_gscale_from_amax(amax_state, gscale=None, stream=None):
     if gscale is None:
         gscale = torch.empty(1, dtype=torch.float32, device=amax_state.device)
     st = load_library().nvfp4_gscale_from_amax(_dev(amax_state, "amax_state"), _dev(gscale, "gscale"),
-                                               _stream_ptr(stream))
+                                               _stream_ptr(stream, amax_state))
     _check("nvfp4_gscale_from_amax", st)
     return gscale
 
@@ -164,7 +176,7 @@ def nvfp4_kv_quantize_fp8(x, scale, out=None, stream=None):
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     st = load_library().nvfp4_kv_quantize_fp8(_dev(x, "x"), _dtype_code(x.dtype), rows, cols, x.stride(0),
-                                              _dev(scale, "scale"), _dev(out, "out"), _stream_ptr(stream))
+                                              _dev(scale, "scale"), _dev(out, "out"), _stream_ptr(stream, x))
     _check("nvfp4_kv_quantize_fp8", st)
     return out
 
@@ -175,7 +187,7 @@ def nvfp4_kv_scale_from_amax(amax_state, scale=None, stream=None):
     if scale is None:
         scale = torch.empty(1, dtype=torch.float32, device=amax_state.device)
     st = load_library().nvfp4_kv_scale_from_amax(_dev(amax_state, "amax_state"), _dev(scale, "scale"),
-                                                 _stream_ptr(stream))
+                                                 _stream_ptr(stream, amax_state))
     _check("nvfp4_kv_scale_from_amax", st)
     return scale
 
@@ -194,7 +206,7 @@ def nvfp4_fuse_rescale(scales, k: int, module_rows, module_gscales, want_lossy: 
     lossy = torch.empty(1, dtype=torch.int64, device=scales.device) if want_lossy else None
     st = load_library().nvfp4_fuse_rescale(_dev(scales, "scales"), int(k), n, ctypes.cast(rows_arr, _P),
                                            ctypes.cast(gs_arr, _P), ctypes.addressof(g_star),
-                                           None if lossy is None else lossy.data_ptr(), _stream_ptr(stream))
+                                           None if lossy is None else lossy.data_ptr(), _stream_ptr(stream, scales))
     _check("nvfp4_fuse_rescale", st)
     return g_star.value, lossy
 
@@ -217,6 +229,6 @@ def nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_dty
     st = load_library().nvfp4_gemm(m, n, k, _dev(a_codes, "a_codes"), _dev(a_scales, "a_scales"),
                                    _dev(a_gscale, "a_gscale"), _dev(w_codes, "w_codes"), _dev(w_scales, "w_scales"),
                                    _dev(w_gscale, "w_gscale"), _dev(out, "out"), _dtype_code(out.dtype),
-                                   out.stride(0), _stream_ptr(stream))
+                                   out.stride(0), _stream_ptr(stream, a_codes))
     _check("nvfp4_gemm", st)
     return out
