@@ -207,6 +207,45 @@ def test_gemm_random_codes(gpu_lib, shape, out_dtype):
     check_gemm(C, ref, bound, out_dtype)
 
 
+def _random_gemm_cases(n, seed):
+    """Seeded random shapes over every GEMM path: 1-64, 65-256 and more rows,
+    N from a handful to the LDS-resident kernel's range, K any multiple of 16
+    up to 8192 (biased to multiples of 128, 256 and 512), scale operands at a
+    byte offset of 0, 4 or 1, and each output dtype."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        m = int(rng.choice([rng.integers(1, 33), rng.integers(1, 65), rng.integers(65, 257), rng.integers(257, 1200)]))
+        big_n = rng.integers(20000, 40000) if m <= 64 else rng.integers(300, 3000)
+        nn = int(rng.choice([rng.integers(1, 300), rng.integers(300, 5000), big_n]))
+        kb = int(rng.choice([16, 128, 256, 512]))
+        k = min(int(kb * rng.integers(1, max(2, 8192 // kb))), 8192)
+        cases.append((m, nn, k, int(rng.choice([0, 0, 0, 4, 1])), str(rng.choice(["f32", "bf16", "f16"]))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_gemm_cases(40, 2026))
+def test_gemm_seeded_random_shapes(gpu_lib, case):
+    M, N, K, off, out_dtype = case
+    rng = np.random.default_rng([31, M, N, K, off])
+    ac, asc = rand_operand(rng, M, K)
+    wc, wsc = rand_operand(rng, N, K)
+    ga, gw = np.float32(rng.uniform(0.5, 300)), np.float32(rng.uniform(100, 3e4))
+    log("gemm random", case)
+
+    def dev_at(a, o):
+        flat = torch.zeros(a.size + 64, dtype=torch.uint8, device="cuda")
+        flat[o:o + a.size] = torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).cuda()
+        return flat[o:o + a.size].view(a.shape)
+
+    c = gpu_lib.nvfp4_gemm(dev_at(ac, 0), dev_at(asc, off), gscale_tensor(ga), dev_at(wc, 0), dev_at(wsc, off),
+                           gscale_tensor(gw),
+                           out_dtype={"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[out_dtype])
+    torch.cuda.synchronize()
+    ref, bound = O.gemm_ref(ac, asc, ga, wc, wsc, gw)
+    check_gemm(c.float().cpu().numpy(), ref, bound, out_dtype)
+
+
 @pytest.mark.parametrize("shape", [(20, 700, 1024), (9, 300, 2048), (32, 500, 5120), (50, 260, 1536), (100, 300, 1024)])
 @pytest.mark.parametrize("scale_offset", [0, 4, 1])
 def test_gemm_offset_scales_strided_output(gpu_lib, shape, scale_offset):
