@@ -115,6 +115,52 @@ def test_quantize_deterministic(gpu_lib):
     assert all(np.array_equal(u, v) for u, v in zip(a, b))
 
 
+def _random_quant_cases(n, seed):
+    """Seeded random quantiser cases: rows 1-600, cols any multiple of 16 up to
+    6384, each input dtype, padded row strides, static or dynamic global scale,
+    and value sets from normal to wide-range (x 2^-20..2^20), tiny, mostly zero
+    and outlier columns."""
+    rng = np.random.default_rng(seed)
+    return [(int(rng.choice([rng.integers(1, 8), rng.integers(8, 600)])), int(16 * rng.integers(1, 400)),
+             str(rng.choice(["f32", "bf16", "f16"])), int(rng.choice([0, 0, 8, 24])),
+             str(rng.choice(["normal", "wide", "tiny", "zeros", "outliers"])), str(rng.choice(["dynamic", "static"])))
+            for _ in range(n)]
+
+
+@pytest.mark.parametrize("case", _random_quant_cases(24, 2027))
+def test_quantize_seeded_random_cases(gpu_lib, case):
+    rows, cols, dt, pad, dist, mode = case
+    rng = np.random.default_rng([32, rows, cols, pad])
+    if dist == "normal":
+        x = rng.standard_normal((rows, cols))
+    elif dist == "wide":
+        x = rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-20, 20, (rows, cols)))
+    elif dist == "tiny":
+        x = rng.standard_normal((rows, cols)) * 1e-6
+    elif dist == "zeros":
+        x = np.where(rng.random((rows, cols)) < 0.7, 0.0, rng.standard_normal((rows, cols)))
+    else:
+        x = rng.standard_normal((rows, cols))
+        x[:, rng.integers(0, cols, 3)] *= 1000
+    x = x.astype(np.float32)
+    if dt == "f16":
+        x = np.clip(x, -60000, 60000).astype(np.float16).astype(np.float32)
+    elif dt == "bf16":
+        x = synth.round_to_bf16(x).astype(np.float32)
+    g = None if mode == "dynamic" else np.float32(rng.uniform(0.1, 1e4))
+    log("quantize random", case)
+    full = np.zeros((rows, cols + pad), np.float32)
+    full[:, :cols] = x
+    t = {"f32": dev_f32, "bf16": dev_bf16, "f16": dev_f16}[dt](full)[:, :cols]
+    gs = gscale_tensor(0.0 if g is None else g)
+    codes, scales = gpu_lib.nvfp4_quantize(t, gs, mode)
+    torch.cuda.synchronize()
+    rc, rs, rg = O.quantize_ref(x, g)
+    assert np.float32(gs.item()) == rg
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
 # ------------------------------------------------------------------ fuse-rescale
 def test_fuse_rescale_matches_oracle(gpu_lib):
     rng = np.random.default_rng(24)
