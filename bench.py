@@ -36,11 +36,13 @@ PEAK_F16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 PEAK_FP4_MFMA_TFLOPS = 10100.0  # MI355X dense fp4 MFMA
 CSRC = os.path.join(ROOT, "nvfp4_w4a4_block_quantize_amd", "csrc")
-# sources of the GEMM kernel each workload's dominant launch runs (traffic counters
-# are tied to these; once they change, the stored counters no longer apply)
+# sources of the kernels each workload's dominant call runs, with the dispatch
+# that picks them (traffic counters are tied to these; once they change, the
+# stored counters no longer apply).  A prefill call may end with a ragged
+# column strip on the decode-shaped kernel.
 KERNEL_SRCS = {
-    "gemm_fast": ("gemm_fast.hip", "gemm_common.h", "nvfp4_device.h"),
-    "gemm_decode": ("gemm_decode.hip", "gemm_common.h", "nvfp4_device.h"),
+    "gemm_fast": ("gemm.hip", "gemm_fast.hip", "gemm_decode.hip", "gemm_common.h", "nvfp4_device.h"),
+    "gemm_decode": ("gemm.hip", "gemm_decode.hip", "gemm_common.h", "nvfp4_device.h"),
     "amax_observe": ("quantize.hip", "nvfp4_device.h"),
     "kv_quantize_fp8": ("kv_quantize.hip", "nvfp4_device.h"),
 }

@@ -305,6 +305,24 @@ bool decode_beats_prefill(int64_t m, int64_t n, int64_t k) {
   return decode_us < prefill_us;
 }
 
+// A ragged last column strip (n % 256 in 1..128) of the prefill grid is a
+// column of tm mostly empty 256x256 tiles.  When those tiles are what opens
+// one more round of tiles on the CUs, that round (the strip alone) costs
+// about a third of a full one (about 0.0205 * k / 3 us: with few CUs busy the
+// chip holds a higher clock).  The decode-shaped kernel then takes the strip
+// instead, in 64-row blocks (grid.y) spread over the whole chip, at about
+// 330 TFLOP/s for these narrow shapes, right after the full columns.
+bool split_ragged_strip(int64_t m, int64_t n, int64_t k) {
+  const int64_t strip = n % 256;
+  if (strip == 0 || strip > 128 || n < 256 || (m + 63) / 64 > 65535) return false;
+  const int64_t cus = device_cu_count();
+  const int64_t tm = (m + 255) / 256, tn = (n + 255) / 256;
+  if ((tm * tn + cus - 1) / cus == (tm * (tn - 1) + cus - 1) / cus) return false;  // the strip adds no round
+  const double tail_us = 0.0205 * (double)k / 3.0;
+  const double strip_us = 2.0 * (double)m * (double)strip * (double)k / 3.3e8;
+  return strip_us < tail_us;
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
@@ -315,6 +333,17 @@ hipError_t launch_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, 
   if (decode && (m <= 64 || !prefill || decode_beats_prefill(m, n, k)))
     return launch_gemm_decode(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype, ldc,
                               stream);
+  if (prefill && split_ragged_strip(m, n, k)) {
+    // full 256-column tiles, then the strip's weight rows and output columns
+    const int64_t n_main = n - n % 256;
+    const hipError_t e = launch_gemm_fast(m, n_main, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c,
+                                          out_dtype, ldc, stream);
+    if (e != hipSuccess) return e;
+    const int64_t es = out_dtype == 0 ? 4 : 2;
+    return launch_gemm_decode(m, n - n_main, k, a_codes, a_scales, a_gscale, w_codes + n_main * (k / 2),
+                              w_scales + n_main * (k / 16), w_gscale, static_cast<uint8_t*>(c) + n_main * es,
+                              out_dtype, ldc, stream);
+  }
   if (prefill)
     return launch_gemm_fast(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype, ldc,
                             stream);

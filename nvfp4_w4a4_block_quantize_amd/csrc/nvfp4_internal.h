@@ -42,7 +42,8 @@ hipError_t launch_gemm_fast(int64_t m, int64_t n, int64_t k, const uint8_t* a_co
                             const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream);
 
 // Decode-shaped path (m <= 256 in blocks of 64 rows, k % 128 == 0, 16-byte aligned codes, 4-byte aligned
-// scales, operands below 2 GiB).
+// scales, operands below 2 GiB).  launch_gemm_decode itself takes any m up to 65535 blocks of 64 rows: the
+// prefill dispatch hands it a ragged last column strip of a large-m GEMM.
 bool gemm_decode_supported(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                            const uint8_t* w_codes, const uint8_t* w_scales);
 hipError_t launch_gemm_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,

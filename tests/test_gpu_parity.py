@@ -236,7 +236,8 @@ GEMM_SHAPES = [(64, 128, 256), (300, 520, 384), (1, 1, 16), (33, 257, 400), (256
                (100, 100, 128), (300, 1000, 640), (1024, 2000, 896), (520, 600, 2176), (2048, 1536, 2176),  # K % 512 != 0
                (32, 600, 2176), (9, 1000, 384), (64, 300, 640), (1, 130, 128), (20, 24577, 384), (48, 5000, 1152),  # K % 256 == 128
                (96, 5000, 5120), (160, 4352, 2176), (250, 1024, 4096), (200, 700, 2176),  # 65-256 rows in 64-row decode blocks
-               (65, 64, 256), (300, 520, 512), (513, 777, 1024), (257, 300, 256), (1000, 1000, 2560), (256, 512, 5120)]
+               (65, 64, 256), (300, 520, 512), (513, 777, 1024), (257, 300, 256), (1000, 1000, 2560), (256, 512, 5120),
+               (512, 32832, 1024), (700, 21800, 640)]  # a ragged last column strip on the decode-shaped kernel (256 CUs)
 
 
 @pytest.mark.parametrize("shape", GEMM_SHAPES)
@@ -292,7 +293,8 @@ def test_gemm_seeded_random_shapes(gpu_lib, case):
     check_gemm(c.float().cpu().numpy(), ref, bound, out_dtype)
 
 
-@pytest.mark.parametrize("shape", [(20, 700, 1024), (9, 300, 2048), (32, 500, 5120), (50, 260, 1536), (100, 300, 1024)])
+@pytest.mark.parametrize("shape", [(20, 700, 1024), (9, 300, 2048), (32, 500, 5120), (50, 260, 1536), (100, 300, 1024),
+                                   (512, 32832, 512)])
 @pytest.mark.parametrize("scale_offset", [0, 4, 1])
 def test_gemm_offset_scales_strided_output(gpu_lib, shape, scale_offset):
     """Scale operands off a 16-byte boundary (legal: the ABI puts no alignment
