@@ -55,7 +55,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None, help="timed steps (default 50; 1000 for decode)")
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed steps first (default 40; 1000 for decode, 200 for calib and kv8): the chip's "
+                        "clock settles over the first 30-40 prefill steps and 600-800 decode steps")
     p.add_argument("--workload", default="gdn", choices=["gdn", "mlp", "decode", "long", "calib", "kv8"],
                    help="calib: the calibration observer over 32K-token batches; kv8: static FP8 K/V "
                         "quantisation of a 32K-token context (both HBM-bound, GB/s)")
@@ -67,7 +69,10 @@ def parse():
                         "activation cast included) on the same shapes")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain device copy of known size (for HBM counter scaling)")
-    return p.parse_args()
+    args = p.parse_args()
+    if args.warmup is None:
+        args.warmup = {"decode": 1000, "calib": 200, "kv8": 200}.get(args.workload, 40)
+    return args
 
 
 def gemm_source_sha(workload):
