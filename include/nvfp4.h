@@ -205,6 +205,12 @@ nvfp4_status nvfp4_fuse_rescale(uint8_t* scales, int64_t k, int32_t n_modules, c
  * is accumulated in fp32.  The kernel, and with it the summation order, is
  * chosen from the shape, the operands' alignment and the device's CU count;
  * for a given choice it is fixed, so repeated calls give identical results.
+ * A prefill-sized call whose last strip of columns (n % 256 of them) would
+ * open another round of 256x256 tiles enqueues two kernels on `stream`: the
+ * tiles over the first n - n % 256 columns, then the decode-shaped kernel
+ * over the strip.  Each output element is computed by exactly one of them.
+ * If the second launch fails, the call returns NVFP4_ERR_DEVICE and the
+ * first part of C may already be written.
  * bf16/f16 outputs are the fp32 result rounded to nearest even.
  *
  * Errors: NULL pointers -> ERR_NULL; m, n, k <= 0, k % 16 != 0, ldc < n ->
