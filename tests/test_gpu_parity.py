@@ -324,10 +324,13 @@ def test_gemm_offset_scales_strided_output(gpu_lib, shape, scale_offset):
     assert torch.all(big[:, N:] == 7.0).item(), "columns past n were written"
 
 
-def test_gemm_f16_output(gpu_lib):
+# the second shape ends in a 40-column strip on the decode-shaped kernel (256 CUs)
+@pytest.mark.parametrize("shape", [(70, 90, 512), (700, 21800, 640)])
+def test_gemm_f16_output(gpu_lib, shape):
+    M, N, K = shape
     rng = np.random.default_rng(27)
-    ac, asc = rand_operand(rng, 70, 512, 0x30, 0x40)
-    wc, wsc = rand_operand(rng, 90, 512, 0x30, 0x40)
+    ac, asc = rand_operand(rng, M, K, 0x30, 0x40)
+    wc, wsc = rand_operand(rng, N, K, 0x30, 0x40)
     C = gemm_gpu(gpu_lib, ac, asc, np.float32(64), wc, wsc, np.float32(64), "f16")
     ref, bound = O.gemm_ref(ac, asc, np.float32(64), wc, wsc, np.float32(64))
     check_gemm(C, ref, bound, "f16")
@@ -356,10 +359,12 @@ def test_gemm_zero_operand_gives_exact_zeros(gpu_lib):
     assert np.all(C == 0)
 
 
-def test_gemm_deterministic(gpu_lib):
+@pytest.mark.parametrize("shape", [(300, 600, 1024), (512, 32832, 1024)])
+def test_gemm_deterministic(gpu_lib, shape):
+    M, N, K = shape
     rng = np.random.default_rng(29)
-    ac, asc = rand_operand(rng, 300, 1024)
-    wc, wsc = rand_operand(rng, 600, 1024)
+    ac, asc = rand_operand(rng, M, K)
+    wc, wsc = rand_operand(rng, N, K)
     a = gemm_gpu(gpu_lib, ac, asc, np.float32(3), wc, wsc, np.float32(5), "f32")
     b = gemm_gpu(gpu_lib, ac, asc, np.float32(3), wc, wsc, np.float32(5), "f32")
     assert np.array_equal(a, b)
