@@ -729,9 +729,15 @@ hipError_t launch_gemm_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_
   // 64 activation rows per workgroup (more in 64-row blocks along grid.y,
   // which stream the same weight rows again, mostly from the caches): one
   // workgroup reads each weight line once for all of them, at 2 waves per
-  // SIMD (3 would spill); 2 weight tiles per workgroup when a block's
-  // workgroups fit one round of slots (2 per CU), else 3
-  if ((n + 31) / 32 <= 2 * (int64_t)device_cu_count())
+  // SIMD (3 would spill).  3 weight tiles per workgroup when that gives every
+  // CU at most one workgroup and 2 would not (with 2, the CUs that get a
+  // second workgroup set the time); else 2 when a block's workgroups fit one
+  // round of slots (2 per CU), else 3
+  const int64_t cus = device_cu_count(), blocks = (m + 63) / 64;
+  if ((n + 31) / 32 * blocks > cus && (n + 47) / 48 * blocks <= cus)
+    return launch_decode_cfg<4, 3, 2>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype,
+                                      ldc, stream);
+  if ((n + 31) / 32 <= 2 * cus)
     return launch_decode_cfg<4, 2, 2>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype,
                                       ldc, stream);
   return launch_decode_cfg<4, 3, 2>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype,
