@@ -539,7 +539,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1",
                           "n_gpus_requested": args.gpus}), flush=True)
         sys.exit(2)
     if args.workload == "calib":

@@ -16,7 +16,7 @@ EXE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
 
 def test_conversion_instructions_match_the_format_rules(gpu_lib):
     if not os.path.exists(EXE):
-        pytest.fail(f"{EXE} is missing: run the build first")
+        pytest.fail(f"{EXE} is missing: build the package first (build.build())")
     print("[case] conformance_cvt", flush=True)
     res = subprocess.run([EXE], capture_output=True, text=True, timeout=100)
     print(res.stdout, flush=True)
