@@ -36,7 +36,8 @@ def prepared(nv, m, n, k, seed):
     return a, ga, wc, ws, gw, ac, asc, c
 
 
-@pytest.mark.parametrize("shape", [(32, 4352, 5120), (512, 1024, 1024)])  # decode kernel, prefill kernel
+# decode kernel; prefill kernel; prefill tiles then a 64-column strip on the decode kernel (two launches, 256 CUs)
+@pytest.mark.parametrize("shape", [(32, 4352, 5120), (512, 1024, 1024), (512, 32832, 1024)])
 def test_graph_replays_match_eager(gpu_lib, shape):
     nv = gpu_lib
     m, n, k = shape
