@@ -524,15 +524,38 @@ def cpu_baseline(lins, rows, workload):
     except AttributeError:
         cores = os.cpu_count()
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    host = host_description()
     if workload == "decode":
         byts = rows * lin.k * 2 + lin.n * (lin.k // 2 + lin.k // 16)
         return {"value": round(byts / dt / 1e9, 4), "unit": "GB/s", "cores": min(cores, threads), "kind": "oracle",
                 "seconds": round(dt, 2),
-                "sample": f"{rows} of {lin.m} rows of {lin.name}: quantise + float64 dequantise-matmul vs full W"}
+                "sample": f"{rows} of {lin.m} rows of {lin.name}: quantise + float64 dequantise-matmul vs full W",
+                **host}
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": min(cores, threads), "kind": "oracle",
             "seconds": round(dt, 2),
             "sample": f"{rows} of {lin.m} activation rows of {lin.name} (N={lin.n}, K={lin.k}): quantise + "
-                      f"float64 dequantise-matmul (plus its |a||w| bound) against the full weight"}
+                      f"float64 dequantise-matmul (plus its |a||w| bound) against the full weight",
+            **host}
+
+
+def host_description():
+    """CPU model and numpy's BLAS build, for the oracle timing."""
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        dep = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{dep.get('name')} {dep.get('version')}".strip()
+    except Exception:
+        pass
+    return {"cpu": cpu, "blas": blas}
 
 
 def main():
