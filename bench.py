@@ -478,7 +478,8 @@ def run(args):
             "gemms": [{"name": lin.name, "M": p.m, "N": p.n, "K": p.k, "modules": p.module_rows,
                        "quant_ms": round(q, 5), "gemm_ms": round(g, 5),
                        "gemm_tflops": round(p.flops() / (g * 1e-3) / 1e12, 2),
-                       "quant_gbs": round(p.quant_bytes() / (q * 1e-3) / 1e9, 1)}
+                       "quant_gbs": round(p.quant_bytes() / (q * 1e-3) / 1e9, 1),
+                       "quant_frac_of_hbm": round(p.quant_bytes() / (q * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
                       for lin, p, q, g in zip(lins, preps, q_ms, g_ms)],
             "a_dtype": lins[0].a_dtype, "c_dtype": "bf16", "act_gscale": "static (calibrated on a separate draw)",
             "weights": "pre-quantised per module, fuse-rescaled, not timed",
