@@ -695,8 +695,8 @@ hipError_t launch_gemm_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_
   // many weight rows each CU streams and by the serial chain of each wave's
   // super-groups, so the kernel is chosen by how many workgroups the shape
   // gives against the chip's slots (3 per CU for the first kernel):
-  //  * the activations resident in LDS, 2 quads of 2 (or 1) weight tiles, when
-  //    that gives between half and one (or at most one) workgroup per CU;
+  //  * the activations resident in LDS, 2 quads of 3, 2 or 1 weight tiles,
+  //    with the fewest tiles that give at most one workgroup per CU;
   //  * else 2 weight tiles per workgroup when that fits one round of slots;
   //  * else the activations resident in LDS (one workgroup of 144 rows per
   //    CU) when it fits, its grid fills one round and the operands are
@@ -704,13 +704,21 @@ hipError_t launch_gemm_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_
   //  * else 3 weight tiles per workgroup (4 for up to 16 rows).
   if (m <= 32) {
     const int64_t cus = device_cu_count();
-    // Activations resident in LDS in smaller workgroups (2 quads, 64 or 32
-    // weight rows) when that gives at most one workgroup per CU: the weight
-    // loads then never queue behind activation loads.  Up to 16384 weight
-    // rows; 9-30% faster than the first kernel at M = 1-32.
+    // Activations resident in LDS in smaller workgroups (2 quads, 96, 64 or
+    // 32 weight rows) when that gives at most one workgroup per CU: the
+    // weight loads then never queue behind activation loads.  Up to 24576
+    // weight rows; 5-30% faster than the first kernel at M = 1-32.
     const bool al2_ok = (reinterpret_cast<uintptr_t>(a_codes) % 16) == 0 &&
                         (reinterpret_cast<uintptr_t>(a_scales) % 16) == 0 &&
                         (reinterpret_cast<uintptr_t>(w_scales) % 16) == 0 && k % kSuperK == 0;
+    if (al2_ok && (n + 95) / 96 <= cus && (n + 63) / 64 > cus) {
+      if (m <= 16 && al_lds_bytes<1, 3, 2>(k) <= kAlLdsBytes)
+        return launch_decode_al<1, 3, 2, kAlD>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c,
+                                               out_dtype, ldc, stream);
+      if (m > 16 && al_lds_bytes<2, 3, 2>(k) <= kAlLdsBytes)
+        return launch_decode_al<2, 3, 2, kAlD>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c,
+                                               out_dtype, ldc, stream);
+    }
     if (al2_ok && (n + 63) / 64 <= cus && 2 * ((n + 63) / 64) > cus) {
       if (m <= 16 && al_lds_bytes<1, 2, 2>(k) <= kAlLdsBytes)
         return launch_decode_al<1, 2, 2, kAlD>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c,
