@@ -699,8 +699,8 @@ hipError_t launch_gemm_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_
   //    with the fewest tiles that give at most one workgroup per CU;
   //  * else 2 weight tiles per workgroup when that fits one round of slots;
   //  * else the activations resident in LDS (one workgroup of 144 rows per
-  //    CU) when it fits, its grid fills one round and the operands are
-  //    16-byte aligned;
+  //    CU) when it fits, the operands are 16-byte aligned and its grid fills
+  //    one round (or, for 17-32 rows, ends in a round at least half full);
   //  * else 3 weight tiles per workgroup (4 for up to 16 rows).
   if (m <= 32) {
     const int64_t cus = device_cu_count();
@@ -744,16 +744,20 @@ hipError_t launch_gemm_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_
     }
     const bool al_ok = (reinterpret_cast<uintptr_t>(a_codes) % 16) == 0 &&
                        (reinterpret_cast<uintptr_t>(a_scales) % 16) == 0 &&
-                       (reinterpret_cast<uintptr_t>(w_scales) % 16) == 0 && k % kSuperK == 0 &&
-                       (n + kAlRowsPerWg - 1) / kAlRowsPerWg <= cus;
+                       (reinterpret_cast<uintptr_t>(w_scales) % 16) == 0 && k % kSuperK == 0;
+    // one round of its one-per-CU grid; for 17-32 rows also several rounds
+    // when the last one is at least half full (an emptier last round, or 16
+    // rows or fewer, is faster on the first kernel)
+    const int64_t al_wgs = (n + kAlRowsPerWg - 1) / kAlRowsPerWg;
+    const bool al_rounds_ok = al_wgs <= cus || (m > 16 && 2 * (al_wgs % cus) >= cus) || (m > 16 && al_wgs % cus == 0);
     if (m <= 16) {
-      if (al_ok && al_lds_bytes<1, kAlT, kAlQ>(k) <= kAlLdsBytes)
+      if (al_ok && al_wgs <= cus && al_lds_bytes<1, kAlT, kAlQ>(k) <= kAlLdsBytes)
         return launch_decode_al<1, kAlT, kAlQ, kAlD>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales,
                                                      w_gscale, c, out_dtype, ldc, stream);
       return launch_decode_cfg<1, 4, 3>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c,
                                         out_dtype, ldc, stream);
     }
-    if (al_ok && al_lds_bytes<2, kAlT, kAlQ>(k) <= kAlLdsBytes)
+    if (al_ok && al_rounds_ok && al_lds_bytes<2, kAlT, kAlQ>(k) <= kAlLdsBytes)
       return launch_decode_al<2, kAlT, kAlQ, kAlD>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale,
                                                    c, out_dtype, ldc, stream);
     return launch_decode_cfg<2, 3, 3>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype,

@@ -240,7 +240,8 @@ GEMM_SHAPES = [(64, 128, 256), (300, 520, 384), (1, 1, 16), (33, 257, 400), (256
                (512, 32832, 1024), (700, 21800, 640), (6000, 8288, 256),  # a ragged last column strip on the decode-shaped kernel (256 CUs)
                (100, 5120, 1024), (40, 10000, 512), (200, 3000, 4096),  # 64-row decode blocks with 3 weight tiles: one workgroup per CU (256 CUs)
                (32, 10240, 512), (9, 9000, 256), (32, 4352, 1024), (5, 640, 768),
-               (32, 17408, 512), (12, 20000, 256)]  # activations in LDS, 2 quads of 1, 2 or 3 weight tiles
+               (32, 17408, 512), (12, 20000, 256),  # activations in LDS, 2 quads of 1, 2 or 3 weight tiles
+               (32, 65536, 256)]  # activations in LDS, 144-row workgroups over two rounds
 
 
 @pytest.mark.parametrize("shape", GEMM_SHAPES)
