@@ -42,7 +42,7 @@ CSRC = os.path.join(ROOT, "nvfp4_w4a4_block_quantize_amd", "csrc")
 # column strip on the decode-shaped kernel.
 KERNEL_SRCS = {
     "gemm_fast": ("gemm.hip", "gemm_fast.hip", "gemm_decode.hip", "gemm_common.h", "nvfp4_device.h"),
-    "gemm_decode": ("gemm.hip", "gemm_decode.hip", "gemm_common.h", "nvfp4_device.h"),
+    "gemm_decode": ("gemm.hip", "gemm_decode.hip", "gemm_stream.hip", "gemm_common.h", "nvfp4_device.h"),
     "amax_observe": ("quantize.hip", "nvfp4_device.h"),
     "kv_quantize_fp8": ("kv_quantize.hip", "nvfp4_device.h"),
 }

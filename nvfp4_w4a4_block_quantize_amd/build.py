@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 CONFORMANCE_PATH = os.path.join(HERE, "conformance_cvt")
 PROBES_PATH = os.path.join(HERE, "libnvfp4_probes.so")
 
-SOURCES = ["nvfp4_abi.cpp", "quantize.hip", "fuse_rescale.hip", "gemm.hip", "gemm_fast.hip", "gemm_decode.hip", "kv_quantize.hip"]
+SOURCES = ["nvfp4_abi.cpp", "quantize.hip", "fuse_rescale.hip", "gemm.hip", "gemm_fast.hip", "gemm_decode.hip", "gemm_stream.hip", "kv_quantize.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

@@ -328,6 +328,10 @@ bool split_ragged_strip(int64_t m, int64_t n, int64_t k) {
 hipError_t launch_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                        const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
                        const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream) {
+  // up to 32 activation rows against a large weight: the weight-streaming kernel
+  if (gemm_stream_supported(m, n, k, a_codes, a_scales, w_codes, w_scales))
+    return launch_gemm_stream(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype, ldc,
+                              stream);
   const bool decode = gemm_decode_supported(m, n, k, a_codes, a_scales, w_codes, w_scales);
   const bool prefill = gemm_fast_supported(m, n, k, a_codes, a_scales, w_codes, w_scales);
   if (decode && (m <= 64 || !prefill || decode_beats_prefill(m, n, k)))

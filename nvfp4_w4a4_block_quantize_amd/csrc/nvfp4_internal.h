@@ -50,6 +50,14 @@ hipError_t launch_gemm_decode(int64_t m, int64_t n, int64_t k, const uint8_t* a_
                               const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
                               const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream);
 
+// Weight-streaming path for up to 32 activation rows: k = 4096 or 5120, 16-byte aligned codes and scales,
+// 80 to 144 weight rows per CU (one workgroup per CU streams a contiguous slab of the weight).
+bool gemm_stream_supported(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
+                           const uint8_t* w_codes, const uint8_t* w_scales);
+hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
+                              const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
+                              const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream);
+
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 

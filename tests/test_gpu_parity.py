@@ -241,7 +241,11 @@ GEMM_SHAPES = [(64, 128, 256), (300, 520, 384), (1, 1, 16), (33, 257, 400), (256
                (100, 5120, 1024), (40, 10000, 512), (200, 3000, 4096),  # 64-row decode blocks with 3 weight tiles: one workgroup per CU (256 CUs)
                (32, 10240, 512), (9, 9000, 256), (32, 4352, 1024), (5, 640, 768),
                (32, 17408, 512), (12, 20000, 256),  # activations in LDS, 2 quads of 1, 2 or 3 weight tiles
-               (32, 65536, 256)]  # activations in LDS, 144-row workgroups over two rounds
+               (32, 65536, 256),  # activations in LDS, 144-row workgroups over two rounds
+               # weight streaming (up to 32 rows, k 4096 or 5120, 80-144 weight rows per CU on 256 CUs):
+               # the decode benchmark's shape, ragged slabs, a last workgroup of one row, 1 and 2 activation tiles
+               (32, 34816, 5120), (1, 20488, 4096), (17, 36864, 4096), (16, 30001, 5120), (32, 25000, 4096),
+               (5, 36863, 5120)]
 
 
 @pytest.mark.parametrize("shape", GEMM_SHAPES)
@@ -298,7 +302,7 @@ def test_gemm_seeded_random_shapes(gpu_lib, case):
 
 
 @pytest.mark.parametrize("shape", [(20, 700, 1024), (9, 300, 2048), (32, 500, 5120), (50, 260, 1536), (100, 300, 1024),
-                                   (512, 32832, 512)])
+                                   (512, 32832, 512), (32, 30000, 5120)])
 @pytest.mark.parametrize("scale_offset", [0, 4, 1])
 def test_gemm_offset_scales_strided_output(gpu_lib, shape, scale_offset):
     """Scale operands off a 16-byte boundary (legal: the ABI puts no alignment
@@ -328,8 +332,8 @@ def test_gemm_offset_scales_strided_output(gpu_lib, shape, scale_offset):
     assert torch.all(big[:, N:] == 7.0).item(), "columns past n were written"
 
 
-# the second shape ends in a 40-column strip on the decode-shaped kernel (256 CUs)
-@pytest.mark.parametrize("shape", [(70, 90, 512), (700, 21800, 640)])
+# the second shape ends in a 40-column strip on the decode-shaped kernel (256 CUs); the third streams the weight
+@pytest.mark.parametrize("shape", [(70, 90, 512), (700, 21800, 640), (24, 30000, 4096)])
 def test_gemm_f16_output(gpu_lib, shape):
     M, N, K = shape
     rng = np.random.default_rng(27)
@@ -338,6 +342,29 @@ def test_gemm_f16_output(gpu_lib, shape):
     C = gemm_gpu(gpu_lib, ac, asc, np.float32(64), wc, wsc, np.float32(64), "f16")
     ref, bound = O.gemm_ref(ac, asc, np.float32(64), wc, wsc, np.float32(64))
     check_gemm(C, ref, bound, "f16")
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("shape", [(20, 24000, 5120), (9, 33001, 4096)])
+def test_gemm_stream_strided_output(gpu_lib, shape, out_dtype):
+    """The weight-streaming kernel writing every output dtype into rows of an
+    odd stride (no 16-byte stores): the columns past n stay untouched."""
+    M, N, K = shape
+    rng = np.random.default_rng([29, M, N, K])
+    ac, asc = rand_operand(rng, M, K)
+    wc, wsc = rand_operand(rng, N, K)
+    ga, gw = np.float32(rng.uniform(0.5, 300)), np.float32(rng.uniform(100, 3e4))
+    log("gemm stream strided", shape, out_dtype)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[out_dtype]
+    ldc = N + 37
+    big = torch.full((M, ldc), 7.0, dtype=tdt, device="cuda")
+    out = big[:, :N]
+    gpu_lib.nvfp4_gemm(t(ac), t(asc), gscale_tensor(ga), t(wc), t(wsc), gscale_tensor(gw), out=out)
+    torch.cuda.synchronize()
+    ref, bound = O.gemm_ref(ac, asc, ga, wc, wsc, gw)
+    check_gemm(out.float().cpu().numpy(), ref, bound, out_dtype)
+    assert torch.all(big[:, N:] == 7.0).item(), "columns past n were written"
 
 
 def test_gemm_extreme_scales(gpu_lib):
@@ -363,7 +390,7 @@ def test_gemm_zero_operand_gives_exact_zeros(gpu_lib):
     assert np.all(C == 0)
 
 
-@pytest.mark.parametrize("shape", [(300, 600, 1024), (512, 32832, 1024)])
+@pytest.mark.parametrize("shape", [(300, 600, 1024), (512, 32832, 1024), (32, 34816, 5120)])
 def test_gemm_deterministic(gpu_lib, shape):
     M, N, K = shape
     rng = np.random.default_rng(29)
