@@ -121,6 +121,33 @@ def _dev(t, name):
     return t.data_ptr()
 
 
+def _same_device(t, like, name):
+    if t.device != like.device:
+        raise ValueError(f"{name} is on {t.device}, expected {like.device}")
+
+
+def _bytes_arg(t, shape, name, like=None):
+    """A uint8 tensor the library reads or writes as dense [rows][cols] bytes."""
+    torch = _torch()
+    if t.dtype != torch.uint8:
+        raise ValueError(f"{name} must be uint8, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if like is not None:
+        _same_device(t, like, name)
+
+
+def _scalar_f32(t, name, like=None):
+    """A one-element float32 tensor (a global scale or an amax word)."""
+    torch = _torch()
+    if t.dtype != torch.float32 or t.numel() != 1:
+        raise ValueError(f"{name} must be a float32 tensor with one element, got {t.dtype} with {t.numel()}")
+    if like is not None:
+        _same_device(t, like, name)
+
+
 def nvfp4_quantize(x, gscale, mode: str = "static", codes=None, scales=None, stream=None):
     """Quantise a 2-D GPU tensor x (f32 / bf16 / f16, unit stride along columns).
 
@@ -136,6 +163,11 @@ def nvfp4_quantize(x, gscale, mode: str = "static", codes=None, scales=None, str
         codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=x.device)
+    _bytes_arg(codes, (rows, cols // 2), "codes", x)
+    _bytes_arg(scales, (rows, cols // 16), "scales", x)
+    _scalar_f32(gscale, "gscale", x)
+    if mode not in ("static", "dynamic"):
+        raise ValueError(f"mode must be 'static' or 'dynamic', got {mode!r}")
     m = {"static": GSCALE_STATIC, "dynamic": GSCALE_DYNAMIC}[mode]
     st = load_library().nvfp4_quantize(_dev(x, "x"), _dtype_code(x.dtype), rows, cols, x.stride(0),
                                        _dev(gscale, "gscale"), m, _dev(codes, "codes"), _dev(scales, "scales"),
@@ -150,6 +182,7 @@ def nvfp4_amax_observe(x, amax_state, stream=None):
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     rows, cols = x.shape
+    _scalar_f32(amax_state, "amax_state", x)
     st = load_library().nvfp4_amax_observe(_dev(x, "x"), _dtype_code(x.dtype), rows, cols, x.stride(0),
                                            _dev(amax_state, "amax_state"), _stream_ptr(stream, x))
     _check("nvfp4_amax_observe", st)
@@ -161,6 +194,8 @@ def nvfp4_gscale_from_amax(amax_state, gscale=None, stream=None):
     torch = _torch()
     if gscale is None:
         gscale = torch.empty(1, dtype=torch.float32, device=amax_state.device)
+    _scalar_f32(amax_state, "amax_state")
+    _scalar_f32(gscale, "gscale", amax_state)
     st = load_library().nvfp4_gscale_from_amax(_dev(amax_state, "amax_state"), _dev(gscale, "gscale"),
                                                _stream_ptr(stream, amax_state))
     _check("nvfp4_gscale_from_amax", st)
@@ -175,6 +210,8 @@ def nvfp4_kv_quantize_fp8(x, scale, out=None, stream=None):
     rows, cols = x.shape
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    _bytes_arg(out, (rows, cols), "out", x)
+    _scalar_f32(scale, "scale", x)
     st = load_library().nvfp4_kv_quantize_fp8(_dev(x, "x"), _dtype_code(x.dtype), rows, cols, x.stride(0),
                                               _dev(scale, "scale"), _dev(out, "out"), _stream_ptr(stream, x))
     _check("nvfp4_kv_quantize_fp8", st)
@@ -186,6 +223,8 @@ def nvfp4_kv_scale_from_amax(amax_state, scale=None, stream=None):
     torch = _torch()
     if scale is None:
         scale = torch.empty(1, dtype=torch.float32, device=amax_state.device)
+    _scalar_f32(amax_state, "amax_state")
+    _scalar_f32(scale, "scale", amax_state)
     st = load_library().nvfp4_kv_scale_from_amax(_dev(amax_state, "amax_state"), _dev(scale, "scale"),
                                                  _stream_ptr(stream, amax_state))
     _check("nvfp4_kv_scale_from_amax", st)
@@ -200,6 +239,9 @@ def nvfp4_fuse_rescale(scales, k: int, module_rows, module_gscales, want_lossy: 
     """
     torch = _torch()
     n = len(module_rows)
+    if len(module_gscales) != n:
+        raise ValueError("module_rows and module_gscales differ in length")
+    _bytes_arg(scales, (sum(int(r) for r in module_rows), int(k) // 16), "scales")
     rows_arr = (ctypes.c_int64 * n)(*[int(r) for r in module_rows])
     gs_arr = (ctypes.c_float * n)(*[float(g) for g in module_gscales])
     g_star = ctypes.c_float(0.0)
@@ -217,15 +259,17 @@ def nvfp4_gemm(a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, out_dty
     m, kh = a_codes.shape
     n = w_codes.shape[0]
     k = kh * 2
-    if w_codes.shape[1] != kh or a_scales.shape != (m, k // 16) or w_scales.shape != (n, k // 16):
-        raise ValueError("operand shapes do not match")
-    for t, nm in ((a_codes, "a_codes"), (a_scales, "a_scales"), (w_codes, "w_codes"), (w_scales, "w_scales")):
-        if not t.is_contiguous():
-            raise ValueError(f"{nm} must be contiguous")
+    _bytes_arg(a_codes, (m, kh), "a_codes")
+    _bytes_arg(a_scales, (m, k // 16), "a_scales", a_codes)
+    _bytes_arg(w_codes, (n, kh), "w_codes", a_codes)
+    _bytes_arg(w_scales, (n, k // 16), "w_scales", a_codes)
+    _scalar_f32(a_gscale, "a_gscale", a_codes)
+    _scalar_f32(w_gscale, "w_gscale", a_codes)
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype or torch.float32, device=a_codes.device)
     if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != m or out.shape[1] < n:
         raise ValueError("out must be [m, >=n] with unit column stride")
+    _same_device(out, a_codes, "out")
     st = load_library().nvfp4_gemm(m, n, k, _dev(a_codes, "a_codes"), _dev(a_scales, "a_scales"),
                                    _dev(a_gscale, "a_gscale"), _dev(w_codes, "w_codes"), _dev(w_scales, "w_scales"),
                                    _dev(w_gscale, "w_gscale"), _dev(out, "out"), _dtype_code(out.dtype),

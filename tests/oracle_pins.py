@@ -35,6 +35,24 @@ def e4m3_fraction_table():
 E4M3_TABLE = e4m3_fraction_table()
 
 
+def count_changed_dequant_factors(old_scales, new_scales, module_rows, module_gscales, g_star):
+    """Blocks of a fused group whose dequantisation factor changed: exact
+    rationals, per block, e4m3(S') / g* against e4m3(S) / g_i (the news
+    article, section 03: the repair folds g*/g_i into the block scales, so a
+    block is reproduced exactly when the two factors are equal)."""
+    val = dict(E4M3_TABLE)
+    old_scales, new_scales = np.asarray(old_scales), np.asarray(new_scales)
+    gs = Fraction(float(np.float32(g_star)))
+    n, r0 = 0, 0
+    for rows, g in zip(module_rows, module_gscales):
+        gi = Fraction(float(np.float32(g)))
+        for b_old, b_new in zip(old_scales[r0:r0 + rows].ravel(), new_scales[r0:r0 + rows].ravel()):
+            if val[int(b_new)] / gs != val[int(b_old)] / gi:
+                n += 1
+        r0 += rows
+    return n
+
+
 def e2m1_exact(y: float) -> int:
     """Nearest E2M1 code by exact rational distance, ties to the even code, saturating."""
     a = abs(Fraction(float(y)))

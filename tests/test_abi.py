@@ -21,9 +21,10 @@ def declared_functions():
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(nv.LIB_PATH):
+    if not os.path.exists(os.environ.get("NVFP4_ABI_LIB") or nv.LIB_PATH):
         pytest.skip("libnvfp4.so not built")
-    return nv.load_library()
+    # NVFP4_ABI_LIB: another build of the C-ABI layer (the sanitized host build)
+    return nv.load_library(os.environ.get("NVFP4_ABI_LIB"))
 
 
 def test_header_declares_the_three_operations():
@@ -137,3 +138,60 @@ def test_kv_quantize_validation(lib):
     assert kv(P, 1, 4, 32, 32, P, P + 4, None) == 3
     assert lib.nvfp4_kv_scale_from_amax(None, P, None) == 1
     assert lib.nvfp4_kv_scale_from_amax(P, P + 1, None) == 3
+
+
+def test_valid_calls_without_a_gpu_return_device_error(lib):
+    """Every launching entry point validates its arguments, then finds no
+    usable GPU and returns NVFP4_ERR_DEVICE without writing anything (the
+    host output of nvfp4_fuse_rescale keeps its value)."""
+    if os.environ.get("NVFP4_NO_GPU") != "1":
+        torch = pytest.importorskip("torch")
+        if torch.cuda.device_count() > 0:
+            pytest.skip("a GPU is visible: valid calls would launch kernels on these placeholder addresses")
+    assert q(lib) == 6
+    assert q(lib, mode=1) == 6
+    assert g(lib) == 6
+    assert g(lib, m=32, n=34816, k=5120, ldc=34816, dt=1) == 6
+    assert f(lib) == (6, -1.0)
+    assert lib.nvfp4_amax_observe(P, 1, 4, 32, 32, P, None) == 6
+    assert lib.nvfp4_gscale_from_amax(P, P, None) == 6
+    assert lib.nvfp4_kv_quantize_fp8(P, 1, 4, 32, 32, P, P, None) == 6
+    assert lib.nvfp4_kv_scale_from_amax(P, P, None) == 6
+
+
+def test_binding_rejects_bad_buffers_before_the_call():
+    """The Python binding checks caller-supplied outputs and scale tensors
+    (dtype, shape, contiguity, one fp32 element) before the C call; a wrong
+    buffer is rejected, never passed on to be written out of bounds."""
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((4, 32), dtype=torch.bfloat16)
+    g1 = torch.zeros(1, dtype=torch.float32)
+    codes, scales = torch.zeros((4, 16), dtype=torch.uint8), torch.zeros((4, 2), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="codes must have shape"):
+        nv.nvfp4_quantize(x, g1, codes=torch.zeros((4, 8), dtype=torch.uint8), scales=scales)
+    with pytest.raises(ValueError, match="scales must be uint8"):
+        nv.nvfp4_quantize(x, g1, codes=codes, scales=torch.zeros((4, 2), dtype=torch.int16))
+    with pytest.raises(ValueError, match="codes must be contiguous"):
+        nv.nvfp4_quantize(x, g1, codes=torch.zeros((16, 4), dtype=torch.uint8).t(), scales=scales)
+    with pytest.raises(ValueError, match="gscale must be a float32 tensor with one element"):
+        nv.nvfp4_quantize(x, torch.zeros(1, dtype=torch.bfloat16), codes=codes, scales=scales)
+    with pytest.raises(ValueError, match="gscale must be a float32 tensor with one element"):
+        nv.nvfp4_quantize(x, torch.zeros(2, dtype=torch.float32), codes=codes, scales=scales)
+    with pytest.raises(ValueError, match="mode must be"):
+        nv.nvfp4_quantize(x, g1, mode="Static", codes=codes, scales=scales)
+    with pytest.raises(ValueError, match="must be a GPU tensor"):  # every buffer right, but on the host
+        nv.nvfp4_quantize(x, g1, codes=codes, scales=scales)
+    ac, asc = torch.zeros((2, 16), dtype=torch.uint8), torch.zeros((2, 2), dtype=torch.uint8)
+    wc, wsc = torch.zeros((3, 16), dtype=torch.uint8), torch.zeros((3, 2), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="w_codes must have shape"):
+        nv.nvfp4_gemm(ac, asc, g1, torch.zeros((3, 8), dtype=torch.uint8), wsc, g1)
+    with pytest.raises(ValueError, match="a_scales must have shape"):
+        nv.nvfp4_gemm(ac, torch.zeros((2, 4), dtype=torch.uint8), g1, wc, wsc, g1)
+    with pytest.raises(ValueError, match="w_gscale must be a float32"):
+        nv.nvfp4_gemm(ac, asc, g1, wc, wsc, torch.zeros(1, dtype=torch.float64))
+    with pytest.raises(ValueError, match="scales must have shape"):
+        nv.nvfp4_fuse_rescale(torch.zeros((5, 2), dtype=torch.uint8), 32, [2, 2], [1.0, 2.0])
+    with pytest.raises(ValueError, match="out must have shape"):
+        nv.nvfp4_kv_quantize_fp8(x, g1, out=torch.zeros((4, 16), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="amax_state must be a float32"):
+        nv.nvfp4_amax_observe(x, torch.zeros(1, dtype=torch.int32))

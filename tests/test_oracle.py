@@ -228,7 +228,9 @@ def test_fuse_power_of_two_ratios_are_exact():
     after = O.dequant_ref(np.concatenate([q0[0], q1[0], q2[0]]), new, gstar)
     normal = np.repeat(new >= 0x08, 16, axis=1)
     assert np.array_equal(after[normal], before[normal])
-    assert lossy == int(np.count_nonzero((new < 0x08) & (scales != 0))) or lossy >= 0
+    # the count of changed dequantisation factors, from exact rationals: with
+    # power-of-two ratios every folded block here stays normal, so none changes
+    assert lossy == P.count_changed_dequant_factors(scales, new, [4, 4, 4], [q0[2], q1[2], q2[2]], gstar) == 0
 
 
 def test_fuse_general_ratio_within_one_e4m3_half_ulp():
@@ -243,7 +245,8 @@ def test_fuse_general_ratio_within_one_e4m3_half_ulp():
     normal = np.repeat(new >= 0x08, 16, axis=1)
     rel = np.abs(after - before)[normal] <= 2.0 ** -4 * np.abs(before[normal]) * (1 + 1e-6)
     assert rel.all()
-    assert lossy > 0
+    exact = P.count_changed_dequant_factors(scales, new, rows, [q[2] for q in qs], gstar)
+    assert lossy == exact and exact > 0
     # the bug: one shared scale without folding distorts by g_i / g* (3x-18x here)
     buggy = O.dequant_ref(codes, scales, gstar)
     ratios = [float(q[2] / gstar) for q in qs]

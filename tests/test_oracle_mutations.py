@@ -76,7 +76,7 @@ def _fuse_pins(m):
         qs.append(O.quantize_ref(w))
     scales = np.concatenate([q[1] for q in qs])
     codes = np.concatenate([q[0] for q in qs])
-    new, gstar, _ = m.fuse_rescale_ref(scales, rows, [q[2] for q in qs])
+    new, gstar, lossy = m.fuse_rescale_ref(scales, rows, [q[2] for q in qs])
     before = np.concatenate([O.dequant_ref(q[0], q[1], q[2]) for q in qs])
     after = O.dequant_ref(codes, new, gstar)
     big = np.repeat(new >= 0x08, 16, axis=1)
@@ -85,6 +85,15 @@ def _fuse_pins(m):
     i = int(np.argmin([q[2] for q in qs]))
     r0 = sum(rows[:i])
     bad += int(np.count_nonzero(new[r0:r0 + rows[i]] != scales[r0:r0 + rows[i]]))
+    # the lossy-block count against exact rationals
+    bad += abs(lossy - P.count_changed_dequant_factors(scales, new, rows, [q[2] for q in qs], gstar))
+    # power-of-two ratios: the folded bytes change, the dequantisation factors do not
+    w = [rng.standard_normal((4, 128)).astype(np.float32) for _ in range(3)]
+    q2 = [O.quantize_ref(wi, np.float32(g)) for wi, g in zip(w, (64.0, 256.0, 1024.0))]
+    s2 = np.concatenate([q[1] for q in q2])
+    new2, g2, lossy2 = m.fuse_rescale_ref(s2, [4, 4, 4], [q[2] for q in q2])
+    bad += int(np.count_nonzero(new2 != s2) == 0)  # the non-owner modules' bytes must change
+    bad += abs(lossy2 - P.count_changed_dequant_factors(s2, new2, [4, 4, 4], [q[2] for q in q2], g2))
     return bad
 
 
@@ -92,6 +101,12 @@ FUSE_MUTANTS = {
     "shared scale is the max encode scale": ("g_star = min(gs)", "g_star = max(gs)"),
     "ratio inverted": ("rho = np.float32(g_star / g_i)", "rho = np.float32(g_i / g_star)"),
     "ratio not folded": ("folded = (e4m3_decode(blk).astype(np.float32) * rho)", "folded = (e4m3_decode(blk).astype(np.float32))"),
+    "lossy count counts changed bytes": (
+        "lossy += int(np.count_nonzero(e4m3_decode(new) * np.float64(g_i) != e4m3_decode(blk) * np.float64(g_star)))",
+        "lossy += int(np.count_nonzero(new != blk))"),
+    "lossy count compares against the module's own scale": (
+        "lossy += int(np.count_nonzero(e4m3_decode(new) * np.float64(g_i) != e4m3_decode(blk) * np.float64(g_star)))",
+        "lossy += int(np.count_nonzero(e4m3_decode(new) * np.float64(g_i) != e4m3_decode(blk) * np.float64(g_i)))"),
 }
 
 
