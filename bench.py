@@ -69,6 +69,9 @@ def parse():
                         "activation cast included) on the same shapes")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain device copy of known size (for HBM counter scaling)")
+    p.add_argument("--no-secondary", action="store_true",
+                   help="gdn only: skip the decode-shaped and MLP workloads and the FP8 comparison that the "
+                        "default line carries beside the headline")
     args = p.parse_args()
     if args.warmup is None:
         args.warmup = {"decode": 1000, "calib": 200, "kv8": 200}.get(args.workload, 40)
@@ -144,6 +147,27 @@ class Prepared:
         return self.m * self.k * self.a.element_size() + self.m * (self.k // 2 + self.k // 16)
 
 
+def fp8_decode_scale(x):
+    """Per-tensor E4M3 decode scale amax / 448 (a 1-element fp32 tensor)."""
+    return (x.float().abs().max() / 448.0).reshape(1).float()
+
+
+def fp8_weight(torch, w, sw):
+    """E4M3 weight bytes: fp32(w / sw) cast to float8_e4m3fn."""
+    return (w.float() / sw).to(torch.float8_e4m3fn)
+
+
+def fp8_activation(torch, a, inv_sa):
+    """E4M3 activation bytes: (a * 1/sa) in the activation's dtype, cast to
+    float8_e4m3fn (what the comparison times every step)."""
+    return (a * inv_sa).to(torch.float8_e4m3fn)
+
+
+def fp8_gemm(torch, a8, w8, sa, sw):
+    """bf16 C = (a8 * sa) @ (w8 * sw)^T by hipBLASLt through torch._scaled_mm."""
+    return torch._scaled_mm(a8, w8.t(), scale_a=sa, scale_b=sw, out_dtype=torch.bfloat16)
+
+
 def fp8_compare(torch, preps, lins, steps, warmup, rotate=1):
     """The recipes the pages compare against keep these GEMMs in FP8 (the news
     article, section 04).  Same shapes and inputs: per-tensor E4M3 scales
@@ -156,20 +180,16 @@ def fp8_compare(torch, preps, lins, steps, warmup, rotate=1):
     try:
         for lin, p in zip(lins, preps):
             dev = p.a.device
-            a = p.a.float()
             w = torch.cat([torch.from_numpy(np.ascontiguousarray(wi, dtype=np.float32)) for _, wi in lin.modules]).to(dev)
-            sa = (a.abs().max() / 448.0).reshape(1).float()
-            sw = (w.abs().max() / 448.0).reshape(1).float()
-            w8s = [(w / sw).to(f8) for _ in range(rotate)]  # copies rotated like the W4A4 weights
-            w8 = w8s[0]
+            sa = fp8_decode_scale(p.a)
+            sw = fp8_decode_scale(w)
+            w8s = [fp8_weight(torch, w, sw) for _ in range(rotate)]  # copies rotated like the W4A4 weights
             a_bf = p.a
             inv_sa = (1.0 / sa).to(a_bf.dtype)
-            del w, a
-            c = torch.empty((p.m, p.n), dtype=torch.bfloat16, device=dev)
+            del w
 
             def one(i):
-                a8 = (a_bf * inv_sa).to(f8)
-                return torch._scaled_mm(a8, w8s[i % rotate].t(), scale_a=sa, scale_b=sw, out_dtype=torch.bfloat16)
+                return fp8_gemm(torch, fp8_activation(torch, a_bf, inv_sa), w8s[i % rotate], sa, sw)
 
             for i in range(warmup):
                 c = one(i)
@@ -182,11 +202,11 @@ def fp8_compare(torch, preps, lins, steps, warmup, rotate=1):
             t1.record()
             torch.cuda.synchronize()
             ms = t0.elapsed_time(t1) / steps
-            a8 = (a_bf * inv_sa).to(f8)
+            a8 = fp8_activation(torch, a_bf, inv_sa)
             torch.cuda.synchronize()
             t0.record()
             for i in range(steps):
-                c = torch._scaled_mm(a8, w8s[i % rotate].t(), scale_a=sa, scale_b=sw, out_dtype=torch.bfloat16)
+                c = fp8_gemm(torch, a8, w8s[i % rotate], sa, sw)
             t1.record()
             torch.cuda.synchronize()
             ms_gemm = t0.elapsed_time(t1) / steps
@@ -196,7 +216,7 @@ def fp8_compare(torch, preps, lins, steps, warmup, rotate=1):
                         "tflops_gemm": round(p.flops() / (ms_gemm * 1e-3) / 1e12, 2),
                         "weight_bytes": p.n * p.k, "gemm_gbs": round(fp8_bytes / (ms_gemm * 1e-3) / 1e9, 1),
                         "weight_copies_rotated": rotate})
-            del w8, w8s, a8, c
+            del w8s, a8, c
     except Exception as e:  # a missing FP8 path is reported, not fatal
         return {"error": f"{type(e).__name__}: {e}"[:300], "done": res}
     return {"kind": "FP8 E4M3 W8A8, per-tensor scales, hipBLASLt via torch._scaled_mm (library baseline)",
@@ -368,16 +388,17 @@ def run_calib(args):
     print(json.dumps(out), flush=True)
 
 
-def run(args):
-    import torch
+WORKLOAD_NAMES = {"gdn": "gdn_fused_in_proj_prefill_8k", "mlp": "mlp_gate_up_down_prefill_8k",
+                  "decode": "decode_gate_up_m32", "long": "attn_qkv_o_prefill_32k"}
 
-    import nvfp4_w4a4_block_quantize_amd as nv
+
+def measure(nv, torch, workload, seed, steps, warmup, fp8=False, copy_cal=False):
+    """One workload's step throughput, per-kernel split and dominant-GEMM
+    roofline.  Returns (result dict, lins) with the device buffers released."""
     from nvfp4_w4a4_block_quantize_amd import synth
 
-    nv.load_library()
-    torch.cuda.init()
-    lins = synth.make_workload(args.workload, seed=args.seed)
-    rotate = 4 if args.workload == "decode" else 1
+    lins = synth.make_workload(workload, seed=seed)
+    rotate = 4 if workload == "decode" else 1
     preps = [Prepared(nv, torch, lin, rotate=rotate) for lin in lins]
     torch.cuda.synchronize()
 
@@ -393,8 +414,7 @@ def run(args):
             if ev is not None:
                 ev[j][2].record()
 
-    steps = args.steps if args.steps is not None else (1000 if args.workload == "decode" else 50)
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
@@ -424,7 +444,7 @@ def run(args):
     # decode-sized launch)
     jd = int(np.argmax([p.flops() for p in preps]))
     pd = preps[jd]
-    reps = min(steps, 200)
+    reps = min(max(steps, 20), 200)
     state = {"i": 0}
 
     def gemm_only():
@@ -435,14 +455,15 @@ def run(args):
     dom_ms = _time_launches(torch, gemm_only, reps)
 
     flops = sum(p.flops() for p in preps)
-    if args.workload == "decode":
+    if workload == "decode":
         p = preps[0]
         step_bytes = p.gemm_bytes() + p.quant_bytes() + p.m * (p.k // 2 + p.k // 16)
         value, unit = step_bytes / (ms_step * 1e-3) / 1e9, "GB/s"
         gb = p.gemm_bytes() / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gb, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gb / PEAK_HBM_GBS, 4), "traffic": load_traffic(args.workload),
-                "kernel": "nvfp4 gemm (decode shape)", "avg_ms": round(dom_ms, 5)}
+                "frac": round(gb / PEAK_HBM_GBS, 4), "traffic": load_traffic(workload),
+                "kernel": "nvfp4 gemm (decode shape)", "avg_ms": round(dom_ms, 5),
+                "bytes_per_launch": p.gemm_bytes()}
         stream = measured_stream_read(torch)
         if stream is not None:
             roof["measured_stream_read_gbs"] = round(stream, 1)
@@ -455,11 +476,10 @@ def run(args):
     else:
         value, unit = flops / (ms_step * 1e-3) / 1e12, "TFLOP/s"
         # dominant kernel: the largest GEMM of the step
-        j = jd
-        ach = preps[j].flops() / (dom_ms * 1e-3) / 1e12
+        ach = pd.flops() / (dom_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_F16_MFMA_TFLOPS, 4), "traffic": load_traffic(args.workload),
-                "kernel": f"nvfp4 gemm {preps[j].m}x{preps[j].n}x{preps[j].k}", "avg_ms": round(dom_ms, 5),
+                "frac": round(ach / PEAK_F16_MFMA_TFLOPS, 4), "traffic": load_traffic(workload),
+                "kernel": f"nvfp4 gemm {pd.m}x{pd.n}x{pd.k}", "avg_ms": round(dom_ms, 5),
                 "frac_of_fp4_peak": round(ach / PEAK_FP4_MFMA_TFLOPS, 4)}
         loop = measured_mfma_peak(torch)
         if loop is not None:
@@ -467,14 +487,11 @@ def run(args):
             roof["frac_of_measured_loop"] = round(ach / loop, 4)
         metric = METRIC
 
-    out = {
-        "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "e2m1xe2m1 decoded exactly to f16, f16 MFMA, f32 accumulate",
-        "data": "synthetic (seeded; no dataset or trained weights)",
+    res = {
+        "metric": metric, "value": round(value, 3), "unit": unit, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
         "config": {
-            "workload": {"gdn": "gdn_fused_in_proj_prefill_8k", "mlp": "mlp_gate_up_down_prefill_8k",
-                         "decode": "decode_gate_up_m32", "long": "attn_qkv_o_prefill_32k"}[args.workload],
+            "workload": WORKLOAD_NAMES[workload],
             "gemms": [{"name": lin.name, "M": p.m, "N": p.n, "K": p.k, "modules": p.module_rows,
                        "quant_ms": round(q, 5), "gemm_ms": round(g, 5),
                        "gemm_tflops": round(p.flops() / (g * 1e-3) / 1e12, 2),
@@ -483,15 +500,76 @@ def run(args):
                       for lin, p, q, g in zip(lins, preps, q_ms, g_ms)],
             "a_dtype": lins[0].a_dtype, "c_dtype": "bf16", "act_gscale": "static (calibrated on a separate draw)",
             "weights": "pre-quantised per module, fuse-rescaled, not timed",
-            "weight_copies_rotated": rotate, "gemm_kernel": WORKLOAD_KERNEL[args.workload],
-            "gemm_source_sha": gemm_source_sha(args.workload),
+            "weight_copies_rotated": rotate, "gemm_kernel": WORKLOAD_KERNEL[workload],
+            "gemm_source_sha": gemm_source_sha(workload),
         },
         "roofline": roof,
     }
-    if args.fp8_compare:
-        out["fp8_w8a8_compare"] = fp8_compare(torch, preps, lins, min(steps, 200), args.warmup, rotate=rotate)
-    if args.copy_calibration:
-        out["copy_calibration_bytes"] = copy_calibration(torch)
+    if fp8:
+        res["fp8_w8a8_compare"] = fp8_compare(torch, preps, lins, min(max(steps, 20), 200), max(warmup, 5),
+                                              rotate=rotate)
+        r0 = res["fp8_w8a8_compare"].get("gemms", [])
+        if r0:
+            res["fp8_w8a8_compare"]["fp8_over_w4a4_gemm_time"] = round(
+                r0[jd]["ms_gemm"] / dom_ms, 4) if jd < len(r0) else None
+    if copy_cal:
+        res["copy_calibration_bytes"] = copy_calibration(torch)
+    del preps
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res, lins
+
+
+def secondary_line(res):
+    """The fields of a secondary workload's result kept in the headline line."""
+    keep = {k: res[k] for k in ("metric", "value", "unit", "steps", "warmup", "ms_per_step")}
+    keep["workload"] = res["config"]["workload"]
+    keep["gemms"] = [{k: g[k] for k in ("name", "M", "N", "K", "quant_ms", "gemm_ms", "gemm_tflops")}
+                     for g in res["config"]["gemms"]]
+    keep["roofline"] = res["roofline"]
+    keep["weight_copies_rotated"] = res["config"]["weight_copies_rotated"]
+    return keep
+
+
+def run(args):
+    import torch
+
+    import nvfp4_w4a4_block_quantize_amd as nv
+
+    nv.load_library()
+    torch.cuda.init()
+    steps = args.steps if args.steps is not None else (1000 if args.workload == "decode" else 50)
+
+    # the north star's other targets, each with its own warm-up and steps, run
+    # before the headline (the chip's clock has then settled for it)
+    secondary = {}
+    if args.workload == "gdn" and not args.no_secondary:
+        dres, _ = measure(nv, torch, "decode", args.seed, 1000, 1000)
+        secondary["decode"] = secondary_line(dres)
+        mres, _ = measure(nv, torch, "mlp", args.seed, 20, 10)
+        secondary["mlp"] = secondary_line(mres)
+
+    res, lins = measure(nv, torch, args.workload, args.seed, steps, args.warmup,
+                        fp8=args.fp8_compare or (args.workload == "gdn" and not args.no_secondary),
+                        copy_cal=args.copy_calibration)
+    out = {
+        "metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "e2m1xe2m1 decoded exactly to f16, f16 MFMA, f32 accumulate",
+        "data": "synthetic (seeded; no dataset or trained weights)",
+        "config": res["config"],
+        "roofline": res["roofline"],
+    }
+    for k in ("fp8_w8a8_compare", "copy_calibration_bytes"):
+        if k in res:
+            out[k] = res[k]
+    if secondary:
+        out["secondary"] = secondary
+    out["timing_order"] = (("secondary workloads (decode, then MLP) with their own warm-up, then " if secondary else "")
+                           + "the headline: --warmup untimed steps, the --steps timed steps (value), a per-kernel "
+                             "event pass, the dominant GEMM alone back to back (roofline), the probes"
+                           + (", the FP8 comparison" if "fp8_w8a8_compare" in res else "")
+                           + ("; then the CPU oracle" if not args.no_cpu_baseline else ""))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(lins, args.cpu_rows, args.workload)
     print(json.dumps(out), flush=True)
