@@ -190,10 +190,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(int64_t M, int64_t N, in
 
   for (int kt = 0; kt < nk; ++kt) {
     uint8_t* st = smem + (kt & 1) * L::stage_bytes;
-    if (kt + 1 < nk) {
-      ldA.load(a_codes, a_scales, m0, M, K, kt + 1, tid);
-      ldW.load(w_codes, w_scales, n0, N, K, kt + 1, tid);
-    }
+    // the next stage's loads (the last iteration loads its own stage again
+    // into the buffer nobody reads after the loop: no branch around the
+    // loader registers, which then stay in registers)
+    const int kn = min(kt + 1, nk - 1);
+    ldA.load(a_codes, a_scales, m0, M, K, kn, tid);
+    ldW.load(w_codes, w_scales, n0, N, K, kn, tid);
     // fragments of this stage: 32 code bytes + one scale word per row
     uint4 ca[FM][2], cw[FN][2];
     half2_t sa[FM][4], sw[FN][4];
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(int64_t M, int64_t N, in
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fw[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) {
+    {
       uint8_t* nx = smem + ((kt + 1) & 1) * L::stage_bytes;
       ldA.store(nx + L::a_codes, reinterpret_cast<uint32_t*>(nx + L::a_scales), tid);
       ldW.store(nx + L::w_codes, reinterpret_cast<uint32_t*>(nx + L::w_scales), tid);
