@@ -69,6 +69,9 @@ def parse():
                         "activation cast included) on the same shapes")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain device copy of known size (for HBM counter scaling)")
+    p.add_argument("--shapes", default=None,
+                   help="comma-separated MxNxK: the GPU time per nvfp4_gemm call on each shape from HIP graph "
+                        "replays (random codes, rotated weight copies) instead of a workload")
     p.add_argument("--no-secondary", action="store_true",
                    help="gdn only: skip the decode-shaped and MLP workloads and the FP8 comparison that the "
                         "default line carries beside the headline")
@@ -637,6 +640,72 @@ def host_description():
     return {"cpu": cpu, "blas": blas}
 
 
+def time_shape(nv, torch, m, n, k, reps=100, min_rotated_bytes=512 << 20, seed=3):
+    """GPU time of one nvfp4_gemm call on MxNxK: `reps` calls captured in one
+    HIP graph, replayed three times after one untimed replay.  A and the
+    weight copies hold random codes and E4M3 scale bytes 0x28-0x47 (scales
+    2^-2 .. 2^1.9); enough weight copies are rotated from call to call that
+    the rotated set reaches `min_rotated_bytes` (2 to 64 copies), so a weight
+    larger than a few MB streams from HBM rather than the 256 MB Infinity
+    Cache.  Timing only: the parity tests check the outputs."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(seed)
+
+    def rnd(rows, cols, lo, hi):
+        return torch.randint(lo, hi, (rows, cols), dtype=torch.uint8, generator=g).to(dev)
+
+    wbytes = n * (k // 2 + k // 16)
+    copies = int(min(64, max(2, -(-min_rotated_bytes // wbytes))))
+    ac, asc = rnd(m, k // 2, 0, 256), rnd(m, k // 16, 0x28, 0x48)
+    ws = [(rnd(n, k // 2, 0, 256), rnd(n, k // 16, 0x28, 0x48)) for _ in range(copies)]
+    ga = torch.full((1,), 0.5, device=dev)
+    gw = torch.full((1,), 2.0, device=dev)
+    c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    for i in range(2 * copies):
+        nv.nvfp4_gemm(ac, asc, ga, ws[i % copies][0], ws[i % copies][1], gw, out=c)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for i in range(reps):
+                nv.nvfp4_gemm(ac, asc, ga, ws[i % copies][0], ws[i % copies][1], gw, out=c)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / (3 * reps) * 1000.0
+    nbytes = (m + n) * (k // 2 + k // 16) + m * n * 2
+    return {"M": m, "N": n, "K": k, "us_per_call": round(us, 3), "weight_copies_rotated": copies,
+            "rotated_weight_mb": round(copies * wbytes / 1e6, 1),
+            "gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "tflops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 2)}
+
+
+def run_shapes(args):
+    import torch
+
+    import nvfp4_w4a4_block_quantize_amd as nv
+
+    nv.load_library()
+    shapes = []
+    for sh in args.shapes.split(","):
+        m, n, k = (int(v) for v in sh.lower().strip().split("x"))
+        if m < 1 or n < 1 or k < 16 or k % 16:
+            raise SystemExit(f"bad shape {sh}: M, N >= 1 and K a positive multiple of 16")
+        shapes.append(time_shape(nv, torch, m, n, k))
+        print(f"[shape] {shapes[-1]}", file=sys.stderr, flush=True)
+    print(json.dumps({"metric": "nvfp4_gemm GPU time per call (HIP graph replays of 100 calls)", "n_gpus": 1,
+                      "data": "synthetic (random codes and scale bytes)", "c_dtype": "bf16", "shapes": shapes}),
+          flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -644,7 +713,9 @@ def main():
         print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1",
                           "n_gpus_requested": args.gpus}), flush=True)
         sys.exit(2)
-    if args.workload == "calib":
+    if args.shapes:
+        run_shapes(args)
+    elif args.workload == "calib":
         run_calib(args)
     elif args.workload == "kv8":
         run_kv8(args)
