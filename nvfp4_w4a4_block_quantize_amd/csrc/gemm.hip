@@ -325,6 +325,33 @@ bool split_ragged_strip(int64_t m, int64_t n, int64_t k) {
   return strip_us < tail_us;
 }
 
+// A call whose 256x256 tiles leave the last round of tiles over the CUs
+// part-empty (MLP down, 8192x5120x17408: 640 tiles, 2.5 rounds of 256) gives
+// the columns of that round to 256x128 tiles, twice as many, so that more CUs
+// take part in it.  Returns how many 256-wide tile columns move to the
+// 128-wide tiles, the fewest that leave the 256x256 part whole rounds, or 0
+// when that is not estimated faster.  Fitted to same-box measurements: a
+// round of 256x128 tiles takes about 0.82 of a round of full tiles (half the
+// MFMAs each, but 1.5 times the decode per MFMA), and a part-empty round of
+// full tiles about 0.95 (the chip clocks higher with fewer CUs busy).  Below
+// K = 1024 a round is too short to pay for the second launch.  Only for n a
+// multiple of 256.
+int64_t half_tile_columns(int64_t m, int64_t n, int64_t k) {
+  if (n % 256 != 0 || k < 1024) return 0;
+  const int64_t cus = device_cu_count();
+  const int64_t tm = (m + 255) / 256, tn = n / 256;
+  if ((tm * tn) % cus == 0) return 0;
+  const double unsplit = (double)((tm * tn) / cus) + 0.95;
+  for (int64_t kk = 1; kk < tn; ++kk) {
+    const int64_t main = tm * (tn - kk);
+    if (main % cus != 0) continue;
+    const int64_t half_rounds = (2 * tm * kk + cus - 1) / cus;
+    const double split = (double)(main / cus) + 0.82 * (double)half_rounds;
+    return split < unsplit ? kk : 0;
+  }
+  return 0;
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
@@ -350,9 +377,22 @@ hipError_t launch_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, 
                               w_scales + n_main * (k / 16), w_gscale, static_cast<uint8_t*>(c) + n_main * es,
                               out_dtype, ldc, stream);
   }
-  if (prefill)
+  if (prefill) {
+    const int64_t kk = half_tile_columns(m, n, k);
+    if (kk > 0) {
+      // whole rounds of 256x256 tiles, then the last columns in 256x128 tiles
+      const int64_t n_main = n - 256 * kk;
+      const hipError_t e = launch_gemm_fast(m, n_main, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale,
+                                            c, out_dtype, ldc, stream);
+      if (e != hipSuccess) return e;
+      const int64_t es = out_dtype == 0 ? 4 : 2;
+      return launch_gemm_fast(m, n - n_main, k, a_codes, a_scales, a_gscale, w_codes + n_main * (k / 2),
+                              w_scales + n_main * (k / 16), w_gscale, static_cast<uint8_t*>(c) + n_main * es,
+                              out_dtype, ldc, stream, 128);
+    }
     return launch_gemm_fast(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, w_gscale, c, out_dtype, ldc,
                             stream);
+  }
   const bool fast = (k % kBK) == 0 && (reinterpret_cast<uintptr_t>(a_codes) % 16) == 0 &&
                     (reinterpret_cast<uintptr_t>(w_codes) % 16) == 0 &&
                     (reinterpret_cast<uintptr_t>(a_scales) % 8) == 0 &&

@@ -3,9 +3,10 @@
 // the W4A4 product of E2M1 codes with E4M3 scales per 16 elements and an FP32
 // global scale per tensor), for k % 128 == 0.
 //
-// Tile: 256 x 256 per workgroup of 4 waves (2 x 2), 128 x 128 per wave = 4 x 4
-// MFMA 32x32x16 tiles, 256 FP32 accumulators per lane.  One stage = 128 K
-// elements = 8 MFMA steps of K 16.
+// Tile: 256 x BN per workgroup of 4 waves (2 x 2), 128 x BN/2 per wave = 4 x
+// BN/64 MFMA 32x32x16 tiles (BN = 256: 256 FP32 accumulators per lane).  One
+// stage = 128 K elements = 8 MFMA steps of K 16.  BN = 128 is for the last
+// round of tiles of a call whose 256 x 256 tiles would leave it part-empty.
 //
 // Data movement.  Global -> LDS uses buffer loads that write LDS directly: one
 // instruction moves 64 lanes x 16 B of codes (or 64 x 4 B of scale words) into
@@ -21,12 +22,15 @@
 //   every step: MFMAs of step s interleaved with the decode of step s+1;
 //   steps 0-5: also two of the global loads of stage kt+3 each;
 //   after step 1: wait for this wave's loads of stage kt+1, one barrier;
-//   steps 2-5: also the LDS reads of stage kt+1's fragments (two per step);
+//   steps 2-5 (2-4 at BN = 128): also the LDS reads of stage kt+1's fragments
+//   (two per step);
 //   step 7 decodes step 0 of stage kt+1.
-// Interleaving is fixed in source: every MFMA is followed by half a fragment's
-// decode (two v_cvt_scalef32_pk_f16_fp4 for this chunk, two v_pk_mul_f16 for
-// the previous chunk, so no multiply waits on the conversion just issued) and
-// a scheduling fence, which keeps the VALU work under the MFMA shadow.
+// Interleaving is fixed in source: the decode of a step is cut in chunks of
+// half a fragment, spread evenly over the step's MFMAs (one per MFMA at
+// BN = 256, one or two at BN = 128); a chunk's two v_cvt_scalef32_pk_f16_fp4
+// are issued after one MFMA and its two v_pk_mul_f16 after the next, so no
+// multiply waits on the conversion just issued, and a scheduling fence after
+// each MFMA's share keeps the VALU work under the MFMA shadow.
 #include "gemm_common.h"
 #include "nvfp4_internal.h"
 
@@ -35,8 +39,7 @@ namespace {
 
 using namespace gemm;
 
-constexpr int BM = 256, BN = 256, TM = 128, TN = 128, FM = 4, FN = 4;
-using L = Layout<BM, BN>;
+constexpr int BM = 256, TM = 128, FM = 4;
 
 typedef __attribute__((address_space(3))) uint8_t* lds_ptr_t;
 typedef __attribute__((address_space(3))) void* lds_void_t;
@@ -123,8 +126,7 @@ struct DirectLoader {
   }
 };
 
-constexpr int kLoadsPerStage = 2 * (DirectLoader<BM>::kCodeInstr + DirectLoader<BM>::kScaleInstr);  // A and W
-
+template <int FN>
 struct Frags {
   uint4 a[FM][2], w[FN][2];
   uint32_t sa[FM], sw[FN];
@@ -135,16 +137,29 @@ __device__ __forceinline__ uint32_t word_of(const uint4 (&q)[2], int s) {
   return (s & 3) == 0 ? v.x : (s & 3) == 1 ? v.y : (s & 3) == 2 ? v.z : v.w;
 }
 
+template <int BN>
 struct Tile {
-  DirectLoader<BM> la;
-  DirectLoader<BN> lw;
+  static constexpr int TN = BN / 2, FN = TN / 32;
+  static constexpr int NF = FM + FN;     // fragments decoded per step
+  static constexpr int NQ = FM * FN;     // MFMAs per step
+  static constexpr int NCH = 2 * NF;     // decode chunks per step
+  using L = Layout<BM, BN>;
+  using LA = DirectLoader<BM>;
+  using LW = DirectLoader<BN>;
+  using Fr = Frags<FN>;
+  static constexpr int kLoads = LA::kCodeInstr + LA::kScaleInstr + LW::kCodeInstr + LW::kScaleInstr;
+  static_assert(kLoads <= 12, "two load slots in each of steps 0-5");
+  // the decode chunks started after MFMA q of a step: [first_chunk(q), first_chunk(q+1))
+  static constexpr int first_chunk(int q) { return (q * NCH + NQ - 1) / NQ; }
+  LA la;
+  LW lw;
   int wave, wm, wn, lr, h;
   float16_t acc[FM][FN];
-  // decoded operands by step parity: F[p][0..3] = A fragments, F[p][4..7] = W
-  half8_t F[2][FM + FN];
+  // decoded operands by step parity: F[p][0..FM-1] = A fragments, F[p][FM..] = W
+  half8_t F[2][NF];
   // fp16 block-scale pairs (S_2b, S_2b+1) of the half stage being decoded
-  half2_t SP[FM + FN];
-  // converted-but-unscaled codes, double-buffered by chunk parity
+  half2_t SP[NF];
+  // converted-but-unscaled codes by chunk parity (at most two chunks wait)
   half2_t T[2][2];
 
   __device__ __forceinline__ void issue_all(lds_ptr_t b, int kt) {
@@ -161,15 +176,15 @@ struct Tile {
   // the g-th of the stage's global loads (interleaved issue)
   template <bool TAIL>
   __device__ __forceinline__ void issue_one(lds_ptr_t b, int kt, int g) {
-    constexpr int C = DirectLoader<BM>::kCodeInstr, S = DirectLoader<BM>::kScaleInstr;
-    if (g < C) la.issue_code(b + L::a_codes, g, kt, wave);
-    else if (g < C + S) la.template issue_scale<TAIL>(b + L::a_scales, g - C, kt, wave);
-    else if (g < 2 * C + S) lw.issue_code(b + L::w_codes, g - C - S, kt, wave);
-    else lw.template issue_scale<TAIL>(b + L::w_scales, g - 2 * C - S, kt, wave);
+    constexpr int CA = LA::kCodeInstr, SA = LA::kScaleInstr, CW = LW::kCodeInstr;
+    if (g < CA) la.issue_code(b + L::a_codes, g, kt, wave);
+    else if (g < CA + SA) la.template issue_scale<TAIL>(b + L::a_scales, g - CA, kt, wave);
+    else if (g < CA + SA + CW) lw.issue_code(b + L::w_codes, g - CA - SA, kt, wave);
+    else lw.template issue_scale<TAIL>(b + L::w_scales, g - CA - SA - CW, kt, wave);
   }
 
-  // LDS reads of fragment f (0..3 = A, 4..7 = W) of the stage held in buffer `st`
-  __device__ __forceinline__ void read_frag(Frags& fr, const uint8_t* st, int f) const {
+  // LDS reads of fragment f (0..FM-1 = A, FM.. = W) of the stage held in buffer `st`
+  __device__ __forceinline__ void read_frag(Fr& fr, const uint8_t* st, int f) const {
     if (f < FM) {
       const int row = wm * TM + f * 32 + lr;
       const uint8_t* base = st + L::a_codes + row * kRowBytes;
@@ -186,11 +201,11 @@ struct Tile {
     }
   }
 
-  // Decode of step s is split in 16 chunks, chunk q = half (q & 1) of fragment
-  // q >> 1.  start(): two code->fp16 conversions into T[q&1] (and, on the
-  // first chunk of a fragment in a half stage, its scale pair).  finish():
-  // the two block-scale multiplies into F[s&1], one chunk later.
-  __device__ __forceinline__ void start(const Frags& src, int s, int q) {
+  // Decode of step s is split in NCH chunks, chunk q = half (q & 1) of
+  // fragment q >> 1.  start(): two code->fp16 conversions into T[q&1] (and,
+  // on the first chunk of a fragment in a half stage, its scale pair).
+  // finish(): the two block-scale multiplies into F[s&1], one MFMA later.
+  __device__ __forceinline__ void start(const Fr& src, int s, int q) {
     const int f = q >> 1, hf = q & 1;
     const uint32_t word = f < FM ? word_of(src.a[f], s) : word_of(src.w[f - FM], s);
     if (hf == 0 && (s & 3) == 0) {
@@ -229,26 +244,41 @@ struct Tile {
   }
 
   // Step S of a stage: the MFMAs of step S while decoding step S+1 of `cur`
-  // (step 0 of `nxt` when S == 7).  Steps 0-5 also issue two of the twelve
-  // global loads of stage kt+3 (slots 5 and 13); steps 2-5, after the barrier,
-  // read two of the next stage's fragments from LDS (slots 0 and 8).
+  // (step 0 of `nxt` when S == 7).  Steps 0-5 also issue two of the stage
+  // kt+3 global loads (after MFMAs NQ/2-3 and NQ-3); from step 2, after the
+  // barrier, two of the next stage's fragments are read from LDS per step
+  // (after MFMAs 0 and NQ/2).
   template <int S, bool TAIL>
-  __device__ __forceinline__ void step_s(const Frags& cur, Frags& nxt, const uint8_t* rd, lds_ptr_t ld, int kt_load) {
+  __device__ __forceinline__ void step_s(const Fr& cur, Fr& nxt, const uint8_t* rd, lds_ptr_t ld, int kt_load) {
 #pragma unroll
-    for (int q = 0; q < FM * FN; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       mfma(S, q);
-      if (q == 0) finish(S, 15);
-      if (q > 0) finish((S + 1) & 7, q - 1);
-      if constexpr (S < 7) {
-        start(cur, S + 1, q);
+      if (q == 0) {
+#pragma unroll
+        for (int c = first_chunk(NQ - 1); c < NCH; ++c) finish(S, c);
       } else {
-        start(nxt, 0, q);
+#pragma unroll
+        for (int c = first_chunk(q - 1); c < first_chunk(q); ++c) finish((S + 1) & 7, c);
       }
-      if constexpr (S >= 2 && S <= 5) {
-        if ((q & 7) == 0) read_frag(nxt, rd, 2 * (S - 2) + (q >> 3));
+#pragma unroll
+      for (int c = first_chunk(q); c < first_chunk(q + 1); ++c) {
+        if constexpr (S < 7) {
+          start(cur, S + 1, c);
+        } else {
+          start(nxt, 0, c);
+        }
+      }
+      if constexpr (S >= 2) {
+        if (q == 0 || q == NQ / 2) {
+          const int f = 2 * (S - 2) + (q == 0 ? 0 : 1);
+          if (f < NF) read_frag(nxt, rd, f);
+        }
       }
       if constexpr (S <= 5) {
-        if ((q & 7) == 5) issue_one<TAIL>(ld, kt_load, 2 * S + (q >> 3));
+        if (q == NQ / 2 - 3 || q == NQ - 3) {
+          const int g = 2 * S + (q < NQ / 2 ? 0 : 1);
+          if (g < kLoads) issue_one<TAIL>(ld, kt_load, g);
+        }
       }
       fence();
     }
@@ -262,16 +292,16 @@ struct Tile {
   // TAIL: some stage this one loads or waits for may lie past the end of K
   // (only in the last iterations of the loop); it then checks.
   template <bool TAIL>
-  __device__ __forceinline__ void stage(int kt, const Frags& cur, Frags& nxt, const uint8_t* rd, lds_ptr_t ld) {
+  __device__ __forceinline__ void stage(int kt, const Fr& cur, Fr& nxt, const uint8_t* rd, lds_ptr_t ld) {
     step_s<0, TAIL>(cur, nxt, rd, ld, kt + 3);
     step_s<1, TAIL>(cur, nxt, rd, ld, kt + 3);
-    // stage kt+1 landed once at most stage kt+2's twelve loads and the four
+    // stage kt+1 landed once at most stage kt+2's loads and the (up to) four
     // of stage kt+3 issued in steps 0-1 are outstanding; a stage past the end
     // of K issues fewer loads (no scale loads), so near the end wait for all
     if (TAIL && kt + 2 >= la.nk) {
       wait_vmcnt<0>();
     } else {
-      wait_vmcnt<kLoadsPerStage + 4>();
+      wait_vmcnt<kLoads + (kLoads < 4 ? kLoads : 4)>();
     }
     lds_barrier();
     step_s<2, TAIL>(cur, nxt, rd, ld, kt + 3);
@@ -308,7 +338,7 @@ __device__ __forceinline__ int xcd_remap(int pid, int total) {
   return xcd * per + min(xcd, rem) + local;
 }
 
-template <int OUT>
+template <int BN, int OUT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64_t N, int64_t K,
                                                                 const uint8_t* __restrict__ a_codes,
                                                                 const uint8_t* __restrict__ a_scales,
@@ -319,6 +349,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64
                                                                 void* __restrict__ c, int64_t ldc, int tiles_m,
                                                                 int tiles_n) {
 #if defined(__HIP_DEVICE_COMPILE__)  // device-only types below; the host pass needs only the launch stub
+  using TileT = Tile<BN>;
+  using L = typename TileT::L;
+  constexpr int TN = TileT::TN, FN = TileT::FN;
   // four stage buffers as separate objects: the compiler can then tell that
   // a read of one never depends on a direct-to-LDS load into another
   __shared__ __attribute__((aligned(1024))) uint8_t buf0[L::stage_bytes];
@@ -327,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64
   __shared__ __attribute__((aligned(1024))) uint8_t buf3[L::stage_bytes];
   const lds_ptr_t l0 = (lds_ptr_t)buf0, l1 = (lds_ptr_t)buf1, l2 = (lds_ptr_t)buf2, l3 = (lds_ptr_t)buf3;
 
-  Tile t;
+  TileT t;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   t.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -362,17 +395,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64
   if (nk < 3) {
     wait_vmcnt<0>();
   } else {
-    wait_vmcnt<2 * kLoadsPerStage>();
+    wait_vmcnt<2 * TileT::kLoads>();
   }
   lds_barrier();
 
-  Frags fx, fy;  // the two fragment register sets, used in turn
+  typename TileT::Fr fx, fy;  // the two fragment register sets, used in turn
 #pragma unroll
-  for (int f = 0; f < FM + FN; ++f) t.read_frag(fx, buf0, f);
+  for (int f = 0; f < TileT::NF; ++f) t.read_frag(fx, buf0, f);
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
+  for (int q = 0; q < TileT::NCH; ++q) {
     t.start(fx, 0, q);
-    if (q < 15) t.finish(0, q);  // chunk 15 is finished in the first slot of stage 0
+    // the chunks of the step's last MFMA are finished in the first slot of stage 0
+    if (q < TileT::first_chunk(TileT::NQ - 1)) t.finish(0, q);
   }
 
   // Four stages per iteration (stages past nk, up to the next multiple of
@@ -386,16 +420,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64
   const int kt_plain = (nk & 3) == 0 ? nk : nk - 6;
   int kt = 0;
   for (; kt < kt_plain; kt += 4) {
-    t.stage<false>(kt + 0, fx, fy, buf1, l3);
-    t.stage<false>(kt + 1, fy, fx, buf2, l0);
-    t.stage<false>(kt + 2, fx, fy, buf3, l1);
-    t.stage<false>(kt + 3, fy, fx, buf0, l2);
+    t.template stage<false>(kt + 0, fx, fy, buf1, l3);
+    t.template stage<false>(kt + 1, fy, fx, buf2, l0);
+    t.template stage<false>(kt + 2, fx, fy, buf3, l1);
+    t.template stage<false>(kt + 3, fy, fx, buf0, l2);
   }
   for (; kt < nk; kt += 4) {
-    t.stage<true>(kt + 0, fx, fy, buf1, l3);
-    t.stage<true>(kt + 1, fy, fx, buf2, l0);
-    t.stage<true>(kt + 2, fx, fy, buf3, l1);
-    t.stage<true>(kt + 3, fy, fx, buf0, l2);
+    t.template stage<true>(kt + 0, fx, fy, buf1, l3);
+    t.template stage<true>(kt + 1, fy, fx, buf2, l0);
+    t.template stage<true>(kt + 2, fx, fy, buf3, l1);
+    t.template stage<true>(kt + 3, fy, fx, buf0, l2);
   }
   wait_vmcnt<0>();  // loads issued for stages past the end
 
@@ -435,6 +469,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64
     __syncthreads();  // every wave is done reading the stage buffers
     constexpr int kPitch = TN * 2 + 16;  // bytes per staged row
     static_assert(64 * kPitch <= L::stage_bytes, "a wave's staging rows fit in one stage buffer");
+    constexpr int kLanesPerRow = TN / 8;                 // 16 bytes (8 outputs) per lane
+    constexpr int kRowsPerPass = 64 / kLanesPerRow;
     // each wave stages in a stage buffer of its own (64 rows x kPitch fit in one)
     uint8_t* const stg = t.wave < 2 ? (t.wave == 0 ? buf0 : buf1) : (t.wave == 2 ? buf2 : buf3);
 #pragma unroll
@@ -455,11 +491,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
       __builtin_amdgcn_wave_barrier();
-      // 64 rows x 256 B: lane reads 16 B; 16 lanes per row, 4 rows per pass
+      // 64 rows x 2 TN bytes: lane reads 16 B; TN/8 lanes per row
 #pragma unroll
-      for (int p = 0; p < 16; ++p) {
-        const int r = p * 4 + (lane >> 4);
-        const int cb = (lane & 15) * 8;  // first of 8 columns
+      for (int p = 0; p < 64 / kRowsPerPass; ++p) {
+        const int r = p * kRowsPerPass + lane / kLanesPerRow;
+        const int cb = (lane % kLanesPerRow) * 8;  // first of 8 columns
         const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kPitch + cb * 2);
         const int64_t row = row_base + half * 64 + r;
         const int64_t col = col_base + cb;
@@ -496,18 +532,29 @@ bool gemm_fast_supported(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes
 
 hipError_t launch_gemm_fast(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                             const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
-                            const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream) {
-  const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + BN - 1) / BN);
+                            const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream,
+                            int tile_n) {
+  const int bn = tile_n == 128 ? 128 : 256;
+  const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + bn - 1) / bn);
   const unsigned grid = (unsigned)tiles_m * (unsigned)tiles_n;
-#define NVFP4_LAUNCH(OUT)                                                                                        \
-  gemm_fast_kernel<OUT><<<grid, kThreads, 0, stream>>>(m, n, k, a_codes, a_scales, a_gscale, w_codes, w_scales, \
-                                                       w_gscale, c, ldc, tiles_m, tiles_n)
-  if (out_dtype == 0)
-    NVFP4_LAUNCH(0);
-  else if (out_dtype == 1)
-    NVFP4_LAUNCH(1);
-  else
-    NVFP4_LAUNCH(2);
+#define NVFP4_LAUNCH(BN, OUT)                                                                                  \
+  gemm_fast_kernel<BN, OUT><<<grid, kThreads, 0, stream>>>(m, n, k, a_codes, a_scales, a_gscale, w_codes,    \
+                                                           w_scales, w_gscale, c, ldc, tiles_m, tiles_n)
+  if (bn == 256) {
+    if (out_dtype == 0)
+      NVFP4_LAUNCH(256, 0);
+    else if (out_dtype == 1)
+      NVFP4_LAUNCH(256, 1);
+    else
+      NVFP4_LAUNCH(256, 2);
+  } else {
+    if (out_dtype == 0)
+      NVFP4_LAUNCH(128, 0);
+    else if (out_dtype == 1)
+      NVFP4_LAUNCH(128, 1);
+    else
+      NVFP4_LAUNCH(128, 2);
+  }
 #undef NVFP4_LAUNCH
   return hipGetLastError();
 }

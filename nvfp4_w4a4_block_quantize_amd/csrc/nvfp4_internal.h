@@ -37,9 +37,11 @@ hipError_t launch_gemm(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, 
 // Main GEMM path (k % 128 == 0, m > 64, 16-byte aligned codes, 4-byte aligned scales, operands below 2 GiB).
 bool gemm_fast_supported(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                          const uint8_t* w_codes, const uint8_t* w_scales);
+// tile_n: 256 (256x256 tiles) or 128 (256x128 tiles, for the last round of a call)
 hipError_t launch_gemm_fast(int64_t m, int64_t n, int64_t k, const uint8_t* a_codes, const uint8_t* a_scales,
                             const float* a_gscale, const uint8_t* w_codes, const uint8_t* w_scales,
-                            const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream);
+                            const float* w_gscale, void* c, int out_dtype, int64_t ldc, hipStream_t stream,
+                            int tile_n = 256);
 
 // Decode-shaped path (m <= 256 in blocks of 64 rows, k % 128 == 0, 16-byte aligned codes, 4-byte aligned
 // scales, operands below 2 GiB).  launch_gemm_decode itself takes any m up to 65535 blocks of 64 rows: the

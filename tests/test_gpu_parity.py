@@ -245,7 +245,10 @@ GEMM_SHAPES = [(64, 128, 256), (300, 520, 384), (1, 1, 16), (33, 257, 400), (256
                # weight streaming (up to 32 rows, k 4096 or 5120, 80-144 weight rows per CU on 256 CUs):
                # the decode benchmark's shape, ragged slabs, a last workgroup of one row, 1 and 2 activation tiles
                (32, 34816, 5120), (1, 20488, 4096), (17, 36864, 4096), (16, 30001, 5120), (32, 25000, 4096),
-               (5, 36863, 5120)]
+               (5, 36863, 5120),
+               # a part-empty last round of 256x256 tiles whose columns go to 256x128 tiles (256 CUs: 320 tiles
+               # -> 256 + 128 columns of 16 row tiles), K a whole number of four-stage groups or not, ragged M
+               (4096, 5120, 1024), (4000, 5120, 1152)]
 
 
 @pytest.mark.parametrize("shape", GEMM_SHAPES)
@@ -302,7 +305,7 @@ def test_gemm_seeded_random_shapes(gpu_lib, case):
 
 
 @pytest.mark.parametrize("shape", [(20, 700, 1024), (9, 300, 2048), (32, 500, 5120), (50, 260, 1536), (100, 300, 1024),
-                                   (512, 32832, 512), (32, 30000, 5120)])
+                                   (512, 32832, 512), (32, 30000, 5120), (4096, 5120, 1024)])
 @pytest.mark.parametrize("scale_offset", [0, 4, 1])
 def test_gemm_offset_scales_strided_output(gpu_lib, shape, scale_offset):
     """Scale operands off a 16-byte boundary (legal: the ABI puts no alignment
