@@ -239,11 +239,11 @@ def copy_calibration(torch):
 
 
 def _probes(torch):
-    """The measurement probes (an MFMA-only loop and a streaming read), built
-    next to the library; None when they are not built."""
+    """The measurement probes (an MFMA-only loop and a streaming read) of
+    bench_probes.hip, built beside this file; None when they are not built."""
     import ctypes
 
-    path = os.path.join(ROOT, "nvfp4_w4a4_block_quantize_amd", "libnvfp4_probes.so")
+    path = os.path.join(ROOT, "libnvfp4_probes.so")
     if not os.path.exists(path):
         return None
     lib = ctypes.CDLL(path)

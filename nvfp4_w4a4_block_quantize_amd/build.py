@@ -17,8 +17,12 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libnvfp4.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-CONFORMANCE_PATH = os.path.join(HERE, "conformance_cvt")
-PROBES_PATH = os.path.join(HERE, "libnvfp4_probes.so")
+# not part of the library: a test program and the bench's measurement probes,
+# each built beside the file that uses it
+CONFORMANCE_SRC = os.path.join(ROOT, "tests", "conformance_cvt.hip")
+CONFORMANCE_PATH = os.path.join(ROOT, "tests", "conformance_cvt")
+PROBES_SRC = os.path.join(ROOT, "bench_probes.hip")
+PROBES_PATH = os.path.join(ROOT, "libnvfp4_probes.so")
 
 SOURCES = ["nvfp4_abi.cpp", "quantize.hip", "fuse_rescale.hip", "gemm.hip", "gemm_fast.hip", "gemm_decode.hip", "gemm_stream.hip", "kv_quantize.hip"]
 
@@ -61,16 +65,16 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB_PATH)
     # conformance check of the conversion instructions the kernels rely on
     # (a standalone program, run by the GPU tests)
-    cmd = [HIPCC, *COMMON_FLAGS, os.path.join(CSRC, "conformance_cvt.hip"), "-o", CONFORMANCE_PATH + ".tmp"]
+    cmd = [HIPCC, *COMMON_FLAGS, CONFORMANCE_SRC, "-o", CONFORMANCE_PATH + ".tmp"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for conformance_cvt.hip:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     os.replace(CONFORMANCE_PATH + ".tmp", CONFORMANCE_PATH)
     # measurement probes for the benchmark (MFMA-only loop, streaming read)
-    cmd = [HIPCC, *COMMON_FLAGS, "-shared", os.path.join(CSRC, "probes.hip"), "-o", PROBES_PATH + ".tmp"]
+    cmd = [HIPCC, *COMMON_FLAGS, "-shared", PROBES_SRC, "-o", PROBES_PATH + ".tmp"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed for probes.hip:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+        raise RuntimeError(f"hipcc failed for bench_probes.hip:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     os.replace(PROBES_PATH + ".tmp", PROBES_PATH)
     if verbose:
         print(f"built {LIB_PATH}, {CONFORMANCE_PATH} and {PROBES_PATH}")

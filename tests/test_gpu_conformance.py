@@ -2,7 +2,7 @@
 rules they implement: the quantiser's E2M1 encoding, the GEMM epilogue's
 fp32 -> bf16 rounding and the FP8 KV quantiser's E4M3 encoding for every
 non-NaN fp32 input, and the GEMM's E2M1 / E4M3 decodes for every code (see
-nvfp4_w4a4_block_quantize_amd/csrc/conformance_cvt.hip)."""
+tests/conformance_cvt.hip, built beside it by the package's build step)."""
 import os
 import subprocess
 
@@ -10,8 +10,7 @@ import pytest
 
 pytestmark = pytest.mark.gpu
 
-EXE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "nvfp4_w4a4_block_quantize_amd",
-                   "conformance_cvt")
+EXE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "conformance_cvt")
 
 
 def test_conversion_instructions_match_the_format_rules(gpu_lib):
