@@ -82,34 +82,49 @@ struct DirectLoader {
   uint32_t scale_off[kScaleInstr];
   int nk;  // stages of K
 
-  __device__ __forceinline__ void init(const uint8_t* codes, const uint8_t* scales, int64_t row0, int64_t rows,
-                                       int64_t k, int wave, int lane) {
+  // this lane's source offsets within a tile's rows (the same for every tile)
+  __device__ __forceinline__ void init_lanes(int64_t k, int wave, int lane) {
     nk = (int)(k / kBK);
-    codes_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)codes, (short)0, (int)(rows * (k / 2)), 0x00020000);
-    scales_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)scales, (short)0, (int)(rows * (k / 16)), 0x00020000);
 #pragma unroll
     for (int i = 0; i < kCodeInstr; ++i) {
       const int p = (wave * kCodeInstr + i) * 64 + lane;  // 16-byte LDS slot of this lane
       const int row = p >> 2;
       const int chunk = (p & 3) ^ swz(row);
-      int64_t r = row0 + row;
-      r = r < rows ? r : rows - 1;  // rows past the matrix repeat the last one (never stored)
-      code_off[i] = (uint32_t)(r * (k / 2) + chunk * 16);
+      code_off[i] = (uint32_t)(row * (k / 2) + chunk * 16);
     }
 #pragma unroll
     for (int i = 0; i < kScaleInstr; ++i) {
       const int p = (wave * kScaleInstr + i) * 64 + lane;  // scale word slot, [half][row]
       const int h = p >= ROWS ? 1 : 0;
       const int row = p - h * ROWS;
-      int64_t r = row0 + row;
-      r = r < rows ? r : rows - 1;
-      scale_off[i] = (uint32_t)(r * (k / 16) + h * 4);
+      scale_off[i] = (uint32_t)(row * (k / 16) + h * 4);
     }
   }
+  // the tile's first row: the resources start there and end with the
+  // matrix, so rows past it read zeros (never stored); rows <= row0 leaves
+  // the resources empty and every load reads nothing
+  __device__ __forceinline__ void target(const uint8_t* codes, const uint8_t* scales, int64_t row0, int64_t rows,
+                                         int64_t k) {
+    const int64_t valid = rows > row0 ? rows - row0 : 0;
+    codes_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(codes + row0 * (k / 2)), (short)0, (int)(valid * (k / 2)),
+                                                   0x00020000);
+    scales_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(scales + row0 * (k / 16)), (short)0,
+                                                    (int)(valid * (k / 16)), 0x00020000);
+  }
+  // The whole matrix instead (the persistent kernel, whose tiles are all
+  // whole): the tile is chosen by `tile_off`, a scalar byte offset of its
+  // first row that every load adds (no record check needed: all rows exist).
+  __device__ __forceinline__ void target_matrix(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                                int64_t k) {
+    codes_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)codes, (short)0, (int)(rows * (k / 2)), 0x00020000);
+    scales_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)scales, (short)0, (int)(rows * (k / 16)), 0x00020000);
+  }
+  // code bytes of the tile's first row; its scale bytes are 1/8 of that
+  uint32_t tile_off = 0;
 
   __device__ __forceinline__ void issue_code(lds_ptr_t lds_codes, int i, int kt, int wave) const {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(codes_rsrc, (lds_void_t)(lds_codes + (wave * kCodeInstr + i) * 1024), 16,
-                                             code_off[i], kt * kRowBytes, 0, 0);
+                                             code_off[i], tile_off + kt * kRowBytes, 0, 0);
   }
   // A stage past the end of K (the loop runs whole groups of four stages)
   // gets zero block scales instead, so every operand it decodes is zero; its
@@ -118,8 +133,8 @@ struct DirectLoader {
   __device__ __forceinline__ void issue_scale(lds_ptr_t lds_scales, int i, int kt, int wave) const {
     const lds_ptr_t dst = lds_scales + (wave * kScaleInstr + i) * 256;
     if (!TAIL || kt < nk) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(scales_rsrc, (lds_void_t)dst, 4, scale_off[i], kt * kBlocksPerStage, 0,
-                                               0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(scales_rsrc, (lds_void_t)dst, 4, scale_off[i],
+                                               (tile_off >> 3) + kt * kBlocksPerStage, 0, 0);
     } else {
       reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(dst)[__lane_id()] = 0u;
     }
@@ -154,6 +169,12 @@ struct Tile {
   LA la;
   LW lw;
   int wave, wm, wn, lr, h;
+  // this lane's LDS read offsets within a stage buffer, for fragment 0 of
+  // each operand: code chunks 2h and 2h+1 of its row (swizzled) and its
+  // scale word.  Fragment f's row is 32 f rows further and has the same
+  // swizzle (it depends on row bits 1-3 only), so its offsets differ by
+  // compile-time constants.
+  uint32_t ra0, ra1, rsa, rw0, rw1, rsw;
   float16_t acc[FM][FN];
   // decoded operands by step parity: F[p][0..FM-1] = A fragments, F[p][FM..] = W
   half8_t F[2][NF];
@@ -183,21 +204,30 @@ struct Tile {
     else lw.template issue_scale<TAIL>(b + L::w_scales, g - CA - SA - CW, kt, wave);
   }
 
+  __device__ __forceinline__ void init_reads() {
+    const int s = swz(lr);
+    const uint32_t arow = (uint32_t)((wm * TM + lr) * kRowBytes), wrow = (uint32_t)((wn * TN + lr) * kRowBytes);
+    ra0 = arow + (uint32_t)(((2 * h) ^ s) << 4);
+    ra1 = arow + (uint32_t)(((2 * h + 1) ^ s) << 4);
+    rsa = (uint32_t)((h * BM + wm * TM + lr) * 4);
+    rw0 = wrow + (uint32_t)(((2 * h) ^ s) << 4);
+    rw1 = wrow + (uint32_t)(((2 * h + 1) ^ s) << 4);
+    rsw = (uint32_t)((h * BN + wn * TN + lr) * 4);
+  }
+
   // LDS reads of fragment f (0..FM-1 = A, FM.. = W) of the stage held in buffer `st`
   __device__ __forceinline__ void read_frag(Fr& fr, const uint8_t* st, int f) const {
     if (f < FM) {
-      const int row = wm * TM + f * 32 + lr;
-      const uint8_t* base = st + L::a_codes + row * kRowBytes;
-      fr.a[f][0] = *reinterpret_cast<const uint4*>(base + (((2 * h) ^ swz(row)) << 4));
-      fr.a[f][1] = *reinterpret_cast<const uint4*>(base + (((2 * h + 1) ^ swz(row)) << 4));
-      fr.sa[f] = reinterpret_cast<const uint32_t*>(st + L::a_scales)[h * BM + row];
+      const uint8_t* base = st + L::a_codes + f * 32 * kRowBytes;
+      fr.a[f][0] = *reinterpret_cast<const uint4*>(base + ra0);
+      fr.a[f][1] = *reinterpret_cast<const uint4*>(base + ra1);
+      fr.sa[f] = *reinterpret_cast<const uint32_t*>(st + L::a_scales + f * 32 * 4 + rsa);
     } else {
       const int j = f - FM;
-      const int row = wn * TN + j * 32 + lr;
-      const uint8_t* base = st + L::w_codes + row * kRowBytes;
-      fr.w[j][0] = *reinterpret_cast<const uint4*>(base + (((2 * h) ^ swz(row)) << 4));
-      fr.w[j][1] = *reinterpret_cast<const uint4*>(base + (((2 * h + 1) ^ swz(row)) << 4));
-      fr.sw[j] = reinterpret_cast<const uint32_t*>(st + L::w_scales)[h * BN + row];
+      const uint8_t* base = st + L::w_codes + j * 32 * kRowBytes;
+      fr.w[j][0] = *reinterpret_cast<const uint4*>(base + rw0);
+      fr.w[j][1] = *reinterpret_cast<const uint4*>(base + rw1);
+      fr.sw[j] = *reinterpret_cast<const uint32_t*>(st + L::w_scales + j * 32 * 4 + rsw);
     }
   }
 
@@ -248,7 +278,9 @@ struct Tile {
   // kt+3 global loads (after MFMAs NQ/2-3 and NQ-3); from step 2, after the
   // barrier, two of the next stage's fragments are read from LDS per step
   // (after MFMAs 0 and NQ/2).
-  template <int S, bool TAIL>
+  // NEXT = false: the stage is the last before an epilogue, and neither
+  // reads the next stage's fragments nor starts decoding them
+  template <int S, bool TAIL, bool NEXT = true>
   __device__ __forceinline__ void step_s(const Fr& cur, Fr& nxt, const uint8_t* rd, lds_ptr_t ld, int kt_load) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
@@ -256,7 +288,7 @@ struct Tile {
       if (q == 0) {
 #pragma unroll
         for (int c = first_chunk(NQ - 1); c < NCH; ++c) finish(S, c);
-      } else {
+      } else if (S < 7 || NEXT) {
 #pragma unroll
         for (int c = first_chunk(q - 1); c < first_chunk(q); ++c) finish((S + 1) & 7, c);
       }
@@ -264,11 +296,11 @@ struct Tile {
       for (int c = first_chunk(q); c < first_chunk(q + 1); ++c) {
         if constexpr (S < 7) {
           start(cur, S + 1, c);
-        } else {
+        } else if constexpr (NEXT) {
           start(nxt, 0, c);
         }
       }
-      if constexpr (S >= 2) {
+      if constexpr (S >= 2 && NEXT) {
         if (q == 0 || q == NQ / 2) {
           const int f = 2 * (S - 2) + (q == 0 ? 0 : 1);
           if (f < NF) read_frag(nxt, rd, f);
@@ -291,10 +323,17 @@ struct Tile {
   // for stages past the end of K fetch data that is never multiplied.
   // TAIL: some stage this one loads or waits for may lie past the end of K
   // (only in the last iterations of the loop); it then checks.
-  template <bool TAIL>
+  template <bool TAIL, bool NEXT = true>
   __device__ __forceinline__ void stage(int kt, const Fr& cur, Fr& nxt, const uint8_t* rd, lds_ptr_t ld) {
-    step_s<0, TAIL>(cur, nxt, rd, ld, kt + 3);
-    step_s<1, TAIL>(cur, nxt, rd, ld, kt + 3);
+    stage_loading<TAIL, NEXT>(kt, kt + 3, cur, nxt, rd, ld);
+  }
+  // the same, with the stage the global loads fetch given apart (the
+  // persistent kernel's last stages of a tile load the next tile's first)
+  template <bool TAIL, bool NEXT = true>
+  __device__ __forceinline__ void stage_loading(int kt, int kl, const Fr& cur, Fr& nxt, const uint8_t* rd,
+                                                lds_ptr_t ld) {
+    step_s<0, TAIL, NEXT>(cur, nxt, rd, ld, kl);
+    step_s<1, TAIL, NEXT>(cur, nxt, rd, ld, kl);
     // stage kt+1 landed once at most stage kt+2's loads and the (up to) four
     // of stage kt+3 issued in steps 0-1 are outstanding; a stage past the end
     // of K issues fewer loads (no scale loads), so near the end wait for all
@@ -304,12 +343,24 @@ struct Tile {
       wait_vmcnt<kLoads + (kLoads < 4 ? kLoads : 4)>();
     }
     lds_barrier();
-    step_s<2, TAIL>(cur, nxt, rd, ld, kt + 3);
-    step_s<3, TAIL>(cur, nxt, rd, ld, kt + 3);
-    step_s<4, TAIL>(cur, nxt, rd, ld, kt + 3);
-    step_s<5, TAIL>(cur, nxt, rd, ld, kt + 3);
-    step_s<6, TAIL>(cur, nxt, rd, ld, kt + 3);
-    step_s<7, TAIL>(cur, nxt, rd, ld, kt + 3);
+    step_s<2, TAIL, NEXT>(cur, nxt, rd, ld, kl);
+    step_s<3, TAIL, NEXT>(cur, nxt, rd, ld, kl);
+    step_s<4, TAIL, NEXT>(cur, nxt, rd, ld, kl);
+    step_s<5, TAIL, NEXT>(cur, nxt, rd, ld, kl);
+    step_s<6, TAIL, NEXT>(cur, nxt, rd, ld, kl);
+    step_s<7, TAIL, NEXT>(cur, nxt, rd, ld, kl);
+  }
+
+  // the fragments of the stage in buffer `st` read, and its step 0 decoded
+  // but for the chunks of the last MFMA (finished in the stage's first step)
+  __device__ __forceinline__ void begin(Fr& fr, const uint8_t* st) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) read_frag(fr, st, f);
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      start(fr, 0, q);
+      if (q < first_chunk(NQ - 1)) finish(0, q);
+    }
   }
 };
 
@@ -337,6 +388,116 @@ __device__ __forceinline__ int xcd_remap(int pid, int total) {
   const int per = total / kXcd, rem = total % kXcd;
   return xcd * per + min(xcd, rem) + local;
 }
+
+#if defined(__HIP_DEVICE_COMPILE__)
+
+// First output row and column of tile `pid` of the grid: grouped tile order
+// (8 tile rows walk the N tiles together) on the XCD-remapped id.
+template <int BN>
+__device__ __forceinline__ void tile_origin(int pid, int tiles_m, int tiles_n, int64_t& m0, int64_t& n0) {
+  const int total = tiles_m * tiles_n;
+  const int tile = xcd_remap(pid, total);
+  constexpr int kGroup = 8;
+  const int group_size = kGroup * tiles_n;
+  const int first_m = (tile / group_size) * kGroup;
+  const int gm_count = min(tiles_m - first_m, kGroup);
+  const int tm = first_m + (tile % group_size) % gm_count;
+  const int tn = (tile % group_size) / gm_count;
+  m0 = (int64_t)tm * BM;
+  n0 = (int64_t)tn * BN;
+}
+
+// Epilogue of one tile: alpha applied once.  16-bit outputs go through the
+// wave's LDS staging area `stg` (PASS_ROWS rows of TN values + 16 B pad, in
+// passes over the wave's 128 rows) so that each lane stores 16 contiguous
+// bytes and TN/8 lanes cover a row segment; fp32 output stores each run of
+// four columns directly (`stg` unused).
+template <int BN, int OUT, int PASS_ROWS = 64>
+__device__ __forceinline__ void store_tile(const Tile<BN>& t, void* __restrict__ c, int64_t ldc, int64_t M,
+                                           int64_t N, int64_t m0, int64_t n0, float alpha, bool vec_ok,
+                                           uint8_t* stg) {
+  constexpr int TN = Tile<BN>::TN, FN = Tile<BN>::FN;
+  // the lane id and what derives from it are computed here (a volatile
+  // block cannot be hoisted out of a caller's tile loop, where the values
+  // would only take registers across the main loop)
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  const int lr = lane & 31, lh = lane >> 5;
+  const int64_t row_base = m0 + t.wm * TM, col_base = n0 + t.wn * TN;
+  if constexpr (OUT == 0) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t row = row_base + i * 32 + lr;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t col = col_base + j * 32 + 8 * g + 4 * lh;
+          const float4 v = make_float4(t.acc[i][j][4 * g] * alpha, t.acc[i][j][4 * g + 1] * alpha,
+                                       t.acc[i][j][4 * g + 2] * alpha, t.acc[i][j][4 * g + 3] * alpha);
+          if (row < M) {
+            float* p = static_cast<float*>(c) + row * ldc + col;
+            if (col + 3 < N && vec_ok) {
+              *reinterpret_cast<float4*>(p) = v;
+            } else {
+              if (col < N) p[0] = v.x;
+              if (col + 1 < N) p[1] = v.y;
+              if (col + 2 < N) p[2] = v.z;
+              if (col + 3 < N) p[3] = v.w;
+            }
+          }
+        }
+    }
+  } else {
+    constexpr int kPitch = TN * 2 + 16;                  // bytes per staged row
+    constexpr int kLanesPerRow = TN / 8;                 // 16 bytes (8 outputs) per lane
+    constexpr int kRowsPerPass = 64 / kLanesPerRow;      // rows one read instruction covers
+    constexpr int kFragsPerPass = PASS_ROWS / 32;
+    static_assert(PASS_ROWS == 32 || PASS_ROWS == 64, "whole 32-row fragments per pass");
+#pragma unroll
+    for (int half = 0; half < FM / kFragsPerPass; ++half) {
+#pragma unroll
+      for (int ii = 0; ii < kFragsPerPass; ++ii) {
+        const int i = kFragsPerPass * half + ii;
+        const int r = ii * 32 + lr;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            uint2 w;
+            w.x = pack2<OUT>(t.acc[i][j][4 * g] * alpha, t.acc[i][j][4 * g + 1] * alpha);
+            w.y = pack2<OUT>(t.acc[i][j][4 * g + 2] * alpha, t.acc[i][j][4 * g + 3] * alpha);
+            *reinterpret_cast<uint2*>(stg + r * kPitch + (j * 32 + 8 * g + 4 * lh) * 2) = w;
+          }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+      __builtin_amdgcn_wave_barrier();
+      // PASS_ROWS rows x 2 TN bytes: lane reads 16 B; TN/8 lanes per row
+#pragma unroll
+      for (int p = 0; p < PASS_ROWS / kRowsPerPass; ++p) {
+        const int r = p * kRowsPerPass + lane / kLanesPerRow;
+        const int cb = (lane % kLanesPerRow) * 8;  // first of 8 columns
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kPitch + cb * 2);
+        const int64_t row = row_base + half * PASS_ROWS + r;
+        const int64_t col = col_base + cb;
+        if (row < M) {
+          uint16_t* q = static_cast<uint16_t*>(c) + row * ldc + col;
+          if (col + 7 < N && vec_ok) {
+            *reinterpret_cast<uint4*>(q) = v;
+          } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (col + e < N) q[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
+#endif  // __HIP_DEVICE_COMPILE__
 
 template <int BN, int OUT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64_t N, int64_t K,
@@ -368,20 +529,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64
   t.wn = t.wave & 1;
   t.lr = lane & 31;
   t.h = lane >> 5;
+  t.init_reads();
 
-  // grouped tile order (8 tile rows walk the N tiles together) on the XCD-remapped id
-  const int total = tiles_m * tiles_n;
-  const int tile = xcd_remap((int)blockIdx.x, total);
-  constexpr int kGroup = 8;
-  const int group_size = kGroup * tiles_n;
-  const int first_m = (tile / group_size) * kGroup;
-  const int gm_count = min(tiles_m - first_m, kGroup);
-  const int tm = first_m + (tile % group_size) % gm_count;
-  const int tn = (tile % group_size) / gm_count;
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  int64_t m0, n0;
+  tile_origin<BN>((int)blockIdx.x, tiles_m, tiles_n, m0, n0);
+  // the global scales are read here, long before the epilogue needs alpha
+  const float alpha = 1.0f / (*a_gscale * *w_gscale);
 
-  t.la.init(a_codes, a_scales, m0, M, K, t.wave, lane);
-  t.lw.init(w_codes, w_scales, n0, N, K, t.wave, lane);
+  t.la.init_lanes(K, t.wave, lane);
+  t.lw.init_lanes(K, t.wave, lane);
+  t.la.target(a_codes, a_scales, m0, M, K);
+  t.lw.target(w_codes, w_scales, n0, N, K);
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -400,14 +558,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64
   lds_barrier();
 
   typename TileT::Fr fx, fy;  // the two fragment register sets, used in turn
-#pragma unroll
-  for (int f = 0; f < TileT::NF; ++f) t.read_frag(fx, buf0, f);
-#pragma unroll
-  for (int q = 0; q < TileT::NCH; ++q) {
-    t.start(fx, 0, q);
-    // the chunks of the step's last MFMA are finished in the first slot of stage 0
-    if (q < TileT::first_chunk(TileT::NQ - 1)) t.finish(0, q);
-  }
+  t.begin(fx, buf0);
 
   // Four stages per iteration (stages past nk, up to the next multiple of
   // four, multiply zeros): two register sets x four LDS buffers, all static.  Stage kt reads stage kt+1 from buffer (kt+1)%4 and
@@ -433,86 +584,141 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64
   }
   wait_vmcnt<0>();  // loads issued for stages past the end
 
-  // Epilogue: alpha applied once.  16-bit outputs go through LDS (rows of
-  // 128 values + 16 B pad, two passes of 64 rows per wave) so that each lane
-  // stores 16 contiguous bytes and 16 lanes cover a 256-byte row segment;
-  // fp32 output stores each run of four columns directly.
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(c) % 16) == 0 && (ldc * (OUT == 0 ? 4 : 2)) % 16 == 0;
+  if constexpr (OUT != 0) __syncthreads();  // every wave is done reading the stage buffers
+  // each wave stages its 16-bit outputs in a stage buffer of its own
+  static_assert(64 * (TN * 2 + 16) <= L::stage_bytes, "a wave's staging rows fit in one stage buffer");
+  uint8_t* const stg = t.wave < 2 ? (t.wave == 0 ? buf0 : buf1) : (t.wave == 2 ? buf2 : buf3);
+  store_tile<BN, OUT>(t, c, ldc, M, N, m0, n0, alpha, vec_ok, stg);
+#endif
+}
+
+// Persistent form of the 256x256 kernel, for K a multiple of 512 (a whole
+// number of groups of four stages) and at least two tiles per workgroup: one
+// workgroup per CU takes tiles pid, pid + G, pid + 2G, ... (G workgroups, a
+// multiple of the 8 XCDs, so that every tile keeps the XCD the one-tile
+// kernel would give it).  The load pipeline runs on across tiles: the last
+// three stages of a tile, whose loads would lie past its end of K, load the
+// next tile's first three stages (moving to the next tile changes only the
+// loaders' buffer resources, scalar registers).  The next tile therefore
+// starts with its operands in LDS, and no workgroup launch separates the
+// tiles.  The tile's last stage reads nothing of the next one, so that the
+// next tile's fragment registers are free during the epilogue; the epilogue
+// stages 16-bit outputs in the buffer of the tile's last stage (32 rows per
+// wave and pass), the one buffer no load targets at that point.
+template <int OUT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_fast_persistent_kernel(
+    int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const float* __restrict__ a_gscale, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales,
+    const float* __restrict__ w_gscale, void* __restrict__ c, int64_t ldc, int tiles_m, int tiles_n) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BN = 256;
+  using TileT = Tile<BN>;
+  using L = typename TileT::L;
+  constexpr int TN = TileT::TN, FN = TileT::FN;
+  __shared__ __attribute__((aligned(1024))) uint8_t buf0[L::stage_bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf1[L::stage_bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf2[L::stage_bytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf3[L::stage_bytes];
+  const lds_ptr_t l0 = (lds_ptr_t)buf0, l1 = (lds_ptr_t)buf1, l2 = (lds_ptr_t)buf2, l3 = (lds_ptr_t)buf3;
+
+  TileT t;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  t.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  t.wm = t.wave >> 1;
+  t.wn = t.wave & 1;
+  t.lr = lane & 31;
+  t.h = lane >> 5;
+  t.init_reads();
+
+  // this tile's and the next one's origins (the next one's is computed a
+  // tile ahead, where the fragment registers are free for the arithmetic)
+  const int total = tiles_m * tiles_n;
+  int pid = (int)blockIdx.x;
+  int64_t m0, n0, nm0 = 0, nn0 = 0;
+  tile_origin<BN>(pid, tiles_m, tiles_n, m0, n0);
+  int next = pid + (int)gridDim.x;
+  bool has_next = next < total;
+  if (has_next) tile_origin<BN>(next, tiles_m, tiles_n, nm0, nn0);
   const float alpha = 1.0f / (*a_gscale * *w_gscale);
   const bool vec_ok = (reinterpret_cast<uintptr_t>(c) % 16) == 0 && (ldc * (OUT == 0 ? 4 : 2)) % 16 == 0;
-  const int64_t row_base = m0 + t.wm * TM, col_base = n0 + t.wn * TN;
-  if constexpr (OUT == 0) {
+  // 16-bit staging: 32 rows per wave in buf3
+  constexpr int kStageRows = 32 * (TN * 2 + 16);
+  static_assert(4 * kStageRows <= L::stage_bytes, "four waves' staging rows fit in one stage buffer");
+  uint8_t* const stg = buf3 + t.wave * kStageRows;
+
+  t.la.init_lanes(K, t.wave, lane);
+  t.lw.init_lanes(K, t.wave, lane);
+  t.la.target_matrix(a_codes, a_scales, M, K);
+  t.lw.target_matrix(w_codes, w_scales, N, K);
+  // byte offsets of this tile's and the next tile's first code rows (with
+  // no next tile, this one's: the last stages then reload its first ones)
+  const uint32_t row_bytes = (uint32_t)(K / 2);
+  uint32_t a_off = (uint32_t)m0 * row_bytes, w_off = (uint32_t)n0 * row_bytes;
+  uint32_t a_next = has_next ? (uint32_t)nm0 * row_bytes : a_off;
+  uint32_t w_next = has_next ? (uint32_t)nn0 * row_bytes : w_off;
+  t.la.tile_off = a_off;
+  t.lw.tile_off = w_off;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int64_t row = row_base + i * 32 + t.lr;
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t col = col_base + j * 32 + 8 * g + 4 * t.h;
-          const float4 v = make_float4(t.acc[i][j][4 * g] * alpha, t.acc[i][j][4 * g + 1] * alpha,
-                                       t.acc[i][j][4 * g + 2] * alpha, t.acc[i][j][4 * g + 3] * alpha);
-          if (row < M) {
-            float* p = static_cast<float*>(c) + row * ldc + col;
-            if (col + 3 < N && vec_ok) {
-              *reinterpret_cast<float4*>(p) = v;
-            } else {
-              if (col < N) p[0] = v.x;
-              if (col + 1 < N) p[1] = v.y;
-              if (col + 2 < N) p[2] = v.z;
-              if (col + 3 < N) p[3] = v.w;
-            }
-          }
-        }
+    for (int j = 0; j < FN; ++j) t.acc[i][j] = float16_t{};
+
+  const int nk = (int)(K / kBK);  // a multiple of 4
+  t.issue_all(l0, 0);
+  t.issue_all(l1, 1);
+  t.issue_all(l2, 2);
+  wait_vmcnt<2 * TileT::kLoads>();  // stage 0 landed
+  lds_barrier();
+
+  typename TileT::Fr fx, fy;  // the two fragment register sets, used in turn
+  t.begin(fx, buf0);
+
+  for (;;) {
+    // The last group of four stages is the loop's last iteration (the same
+    // code, so the same address registers): after its first stage, which
+    // loads the tile's last stage, the loaders move to the next tile, and
+    // stages nk-3 .. nk-1 load its stages 0 .. 2.  The tile's last stage
+    // reads the next tile's first stage and decodes its first step, as
+    // within a tile.
+    for (int kt = 0; kt < nk; kt += 4) {
+      t.la.tile_off = a_off;
+      t.lw.tile_off = w_off;
+      t.template stage_loading<false>(kt, kt + 3, fx, fy, buf1, l3);
+      const bool last = kt + 4 == nk;
+      t.la.tile_off = last ? a_next : a_off;
+      t.lw.tile_off = last ? w_next : w_off;
+      const int kl = last ? 0 : kt + 4;
+      t.template stage_loading<false>(kt + 1, kl, fy, fx, buf2, l0);
+      t.template stage_loading<false>(kt + 2, kl + 1, fx, fy, buf3, l1);
+      t.template stage_loading<false>(kt + 3, kl + 2, fy, fx, buf0, l2);
     }
-  } else {
-    wait_vmcnt<0>();  // loads issued for stages past the end may still target LDS
-    __syncthreads();  // every wave is done reading the stage buffers
-    constexpr int kPitch = TN * 2 + 16;  // bytes per staged row
-    static_assert(64 * kPitch <= L::stage_bytes, "a wave's staging rows fit in one stage buffer");
-    constexpr int kLanesPerRow = TN / 8;                 // 16 bytes (8 outputs) per lane
-    constexpr int kRowsPerPass = 64 / kLanesPerRow;
-    // each wave stages in a stage buffer of its own (64 rows x kPitch fit in one)
-    uint8_t* const stg = t.wave < 2 ? (t.wave == 0 ? buf0 : buf1) : (t.wave == 2 ? buf2 : buf3);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-#pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int i = 2 * half + ii;
-        const int r = ii * 32 + t.lr;
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            uint2 w;
-            w.x = pack2<OUT>(t.acc[i][j][4 * g] * alpha, t.acc[i][j][4 * g + 1] * alpha);
-            w.y = pack2<OUT>(t.acc[i][j][4 * g + 2] * alpha, t.acc[i][j][4 * g + 3] * alpha);
-            *reinterpret_cast<uint2*>(stg + r * kPitch + (j * 32 + 8 * g + 4 * t.h) * 2) = w;
-          }
-      }
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
-      __builtin_amdgcn_wave_barrier();
-      // 64 rows x 2 TN bytes: lane reads 16 B; TN/8 lanes per row
-#pragma unroll
-      for (int p = 0; p < 64 / kRowsPerPass; ++p) {
-        const int r = p * kRowsPerPass + lane / kLanesPerRow;
-        const int cb = (lane % kLanesPerRow) * 8;  // first of 8 columns
-        const uint4 v = *reinterpret_cast<const uint4*>(stg + r * kPitch + cb * 2);
-        const int64_t row = row_base + half * 64 + r;
-        const int64_t col = col_base + cb;
-        if (row < M) {
-          uint16_t* q = static_cast<uint16_t*>(c) + row * ldc + col;
-          if (col + 7 < N && vec_ok) {
-            *reinterpret_cast<uint4*>(q) = v;
-          } else {
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (col + e < N) q[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-          }
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
+
+    // buf3 held the tile's last stage, read by every wave before the barrier
+    // of stage nk-1; loads into buf1 and buf2 (and the next tile's first
+    // stage, landed, in buf0) stay where they are
+    store_tile<BN, OUT, 32>(t, c, ldc, M, N, m0, n0, alpha, vec_ok, stg);
+    if (!has_next) {
+      wait_vmcnt<0>();  // the last three stages' loads (this tile's first ones again) still target LDS
+      break;
     }
+    // the staging reads are done before the next tile's first stage loads into buf3
+    if constexpr (OUT != 0) lds_barrier();
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) t.acc[i][j] = float16_t{};
+    pid = next;
+    m0 = nm0;
+    n0 = nn0;
+    a_off = a_next;
+    w_off = w_next;
+    next = pid + (int)gridDim.x;
+    has_next = next < total;
+    if (has_next) tile_origin<BN>(next, tiles_m, tiles_n, nm0, nn0);
+    a_next = has_next ? (uint32_t)nm0 * row_bytes : a_off;
+    w_next = has_next ? (uint32_t)nn0 * row_bytes : w_off;
   }
 #endif
 }
@@ -537,6 +743,24 @@ hipError_t launch_gemm_fast(int64_t m, int64_t n, int64_t k, const uint8_t* a_co
   const int bn = tile_n == 128 ? 128 : 256;
   const int tiles_m = (int)((m + BM - 1) / BM), tiles_n = (int)((n + bn - 1) / bn);
   const unsigned grid = (unsigned)tiles_m * (unsigned)tiles_n;
+  // whole 256x256 tiles only, at least three per CU, and K a whole number of
+  // four-stage groups: the persistent form, one workgroup per CU (a whole
+  // number per XCD).  With about two tiles per CU it measured no faster.
+  const int cus = device_cu_count();
+  if (bn == 256 && m % BM == 0 && n % 256 == 0 && (k / kBK) % 4 == 0 && cus >= 8 && cus % 8 == 0 &&
+      (int64_t)grid >= 3 * (int64_t)cus) {
+    const unsigned pgrid = (unsigned)cus;
+    if (out_dtype == 0)
+      gemm_fast_persistent_kernel<0><<<pgrid, kThreads, 0, stream>>>(m, n, k, a_codes, a_scales, a_gscale, w_codes,
+                                                                     w_scales, w_gscale, c, ldc, tiles_m, tiles_n);
+    else if (out_dtype == 1)
+      gemm_fast_persistent_kernel<1><<<pgrid, kThreads, 0, stream>>>(m, n, k, a_codes, a_scales, a_gscale, w_codes,
+                                                                     w_scales, w_gscale, c, ldc, tiles_m, tiles_n);
+    else
+      gemm_fast_persistent_kernel<2><<<pgrid, kThreads, 0, stream>>>(m, n, k, a_codes, a_scales, a_gscale, w_codes,
+                                                                     w_scales, w_gscale, c, ldc, tiles_m, tiles_n);
+    return hipGetLastError();
+  }
 #define NVFP4_LAUNCH(BN, OUT)                                                                                  \
   gemm_fast_kernel<BN, OUT><<<grid, kThreads, 0, stream>>>(m, n, k, a_codes, a_scales, a_gscale, w_codes,    \
                                                            w_scales, w_gscale, c, ldc, tiles_m, tiles_n)

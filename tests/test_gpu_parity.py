@@ -265,6 +265,27 @@ def test_gemm_random_codes(gpu_lib, shape, out_dtype):
     check_gemm(C, ref, bound, out_dtype)
 
 
+# the persistent form of the prefill kernel (whole 256x256 tiles, at least three per CU, K a multiple of
+# 512; on 256 CUs): the fewest stages (K = 512, the last group of four the only one) at exactly three
+# tiles per workgroup, and tile counts that are not a whole number of rounds (some workgroups take one
+# tile more); the ragged shape has as many tiles but runs the one-tile kernel
+PERSISTENT_SHAPES = [(4096, 12288, 512), (6144, 8448, 1024), (3072, 16640, 1536), (4000, 8400, 1024)]
+
+
+@pytest.mark.parametrize("shape", PERSISTENT_SHAPES)
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
+def test_gemm_persistent_prefill(gpu_lib, shape, out_dtype):
+    M, N, K = shape
+    rng = np.random.default_rng([33, M, N, K])
+    ac, asc = rand_operand(rng, M, K)
+    wc, wsc = rand_operand(rng, N, K)
+    ga, gw = np.float32(rng.uniform(0.5, 300)), np.float32(rng.uniform(100, 3e4))
+    log("gemm persistent", shape, out_dtype)
+    C = gemm_gpu(gpu_lib, ac, asc, ga, wc, wsc, gw, out_dtype)
+    ref, bound = O.gemm_ref(ac, asc, ga, wc, wsc, gw)
+    check_gemm(C, ref, bound, out_dtype)
+
+
 def _random_gemm_cases(n, seed):
     """Seeded random shapes over every GEMM path: 1-64, 65-256 and more rows,
     N from a handful to the LDS-resident kernel's range, K any multiple of 16
@@ -305,7 +326,8 @@ def test_gemm_seeded_random_shapes(gpu_lib, case):
 
 
 @pytest.mark.parametrize("shape", [(20, 700, 1024), (9, 300, 2048), (32, 500, 5120), (50, 260, 1536), (100, 300, 1024),
-                                   (512, 32832, 512), (32, 30000, 5120), (4096, 5120, 1024)])
+                                   (512, 32832, 512), (32, 30000, 5120), (4096, 5120, 1024), (4000, 8400, 1024),
+                                   (6144, 8448, 1024)])
 @pytest.mark.parametrize("scale_offset", [0, 4, 1])
 def test_gemm_offset_scales_strided_output(gpu_lib, shape, scale_offset):
     """Scale operands off a 16-byte boundary (legal: the ABI puts no alignment
@@ -393,7 +415,7 @@ def test_gemm_zero_operand_gives_exact_zeros(gpu_lib):
     assert np.all(C == 0)
 
 
-@pytest.mark.parametrize("shape", [(300, 600, 1024), (512, 32832, 1024), (32, 34816, 5120)])
+@pytest.mark.parametrize("shape", [(300, 600, 1024), (512, 32832, 1024), (32, 34816, 5120), (3072, 16640, 1536)])
 def test_gemm_deterministic(gpu_lib, shape):
     M, N, K = shape
     rng = np.random.default_rng(29)
