@@ -286,6 +286,28 @@ def test_gemm_persistent_prefill(gpu_lib, shape, out_dtype):
     check_gemm(C, ref, bound, out_dtype)
 
 
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
+def test_gemm_persistent_prefill_strided_output(gpu_lib, out_dtype):
+    """The persistent prefill kernel writing every output dtype into rows of an
+    odd stride (no 16-byte stores): the columns past n stay untouched."""
+    M, N, K = 4096, 12288, 1024
+    rng = np.random.default_rng([34, M, N, K])
+    ac, asc = rand_operand(rng, M, K)
+    wc, wsc = rand_operand(rng, N, K)
+    ga, gw = np.float32(rng.uniform(0.5, 300)), np.float32(rng.uniform(100, 3e4))
+    log("gemm persistent strided", (M, N, K), out_dtype)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[out_dtype]
+    ldc = N + 37
+    big = torch.full((M, ldc), 7.0, dtype=tdt, device="cuda")
+    out = big[:, :N]
+    gpu_lib.nvfp4_gemm(t(ac), t(asc), gscale_tensor(ga), t(wc), t(wsc), gscale_tensor(gw), out=out)
+    torch.cuda.synchronize()
+    ref, bound = O.gemm_ref(ac, asc, ga, wc, wsc, gw)
+    check_gemm(out.float().cpu().numpy(), ref, bound, out_dtype)
+    assert torch.all(big[:, N:] == 7.0).item(), "columns past n were written"
+
+
 def _random_gemm_cases(n, seed):
     """Seeded random shapes over every GEMM path: 1-64, 65-256 and more rows,
     N from a handful to the LDS-resident kernel's range, K any multiple of 16
