@@ -543,8 +543,8 @@ def run(args):
     torch.cuda.init()
     steps = args.steps if args.steps is not None else (1000 if args.workload == "decode" else 50)
 
-    # the benchmark spec's other targets, each with its own warm-up and steps, run
-    # before the headline (the chip's clock has then settled for it)
+    # the decode-shaped and MLP workloads, each with its own warm-up and steps,
+    # run before the headline (the chip's clock has then settled for it)
     secondary = {}
     if args.workload == "gdn" and not args.no_secondary:
         dres, _ = measure(nv, torch, "decode", args.seed, 1000, 1000)
