@@ -268,8 +268,10 @@ def test_gemm_random_codes(gpu_lib, shape, out_dtype):
 # the persistent form of the prefill kernel (whole 256x256 tiles, at least three per CU, K a multiple of
 # 512; on 256 CUs): the fewest stages (K = 512, the last group of four the only one) at exactly three
 # tiles per workgroup, and tile counts that are not a whole number of rounds (some workgroups take one
-# tile more); the ragged shape has as many tiles but runs the one-tile kernel
-PERSISTENT_SHAPES = [(4096, 12288, 512), (6144, 8448, 1024), (3072, 16640, 1536), (4000, 8400, 1024)]
+# tile more); a single row of 769 tiles (a count that is not a multiple of the 8 XCDs); the ragged
+# shape has as many tiles but runs the one-tile kernel
+PERSISTENT_SHAPES = [(4096, 12288, 512), (6144, 8448, 1024), (3072, 16640, 1536), (256, 196864, 512),
+                     (4000, 8400, 1024)]
 
 
 @pytest.mark.parametrize("shape", PERSISTENT_SHAPES)
