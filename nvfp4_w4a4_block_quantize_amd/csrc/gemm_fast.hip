@@ -12,9 +12,9 @@
 // instruction moves 64 lanes x 16 B of codes (or 64 x 4 B of scale words) into
 // 1 KiB (256 B) of consecutive LDS, each lane fetching the global chunk that
 // belongs at its slot; this produces the swizzled code rows and the
-// [half][row] scale words without staging registers.  Two LDS buffers; the
-// fragments of a stage (32 code bytes + one scale word per row and lane half)
-// are double-buffered in registers; four LDS stage buffers (separate objects,
+// [half][row] scale words without staging registers.  The fragments of a
+// stage (32 code bytes + one scale word per row and lane half) are
+// double-buffered in registers, and four LDS stage buffers (separate objects,
 // so the compiler never waits on a direct load into one before reading
 // another) keep the loads of stage kt+3 in flight while stage kt runs.
 //
@@ -561,9 +561,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64
   t.begin(fx, buf0);
 
   // Four stages per iteration (stages past nk, up to the next multiple of
-  // four, multiply zeros): two register sets x four LDS buffers, all static.  Stage kt reads stage kt+1 from buffer (kt+1)%4 and
-  // loads stage kt+3 into buffer (kt+3)%4, which held stage kt-1 (already in
-  // every wave's registers by the barrier of stage kt).
+  // four, multiply zeros): two register sets x four LDS buffers, all static.
+  // Stage kt reads stage kt+1 from buffer (kt+1)%4 and loads stage kt+3 into
+  // buffer (kt+3)%4, which held stage kt-1 (already in every wave's registers
+  // by the barrier of stage kt).
   // Iterations whose loads (stages kt+3 .. kt+6) all lie inside K take no
   // checks, and so does every iteration when K is a whole number of groups
   // of four stages (then no stage past the end is multiplied); otherwise the
@@ -593,19 +594,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_kernel(int64_t M, int64
 #endif
 }
 
-// Persistent form of the 256x256 kernel, for K a multiple of 512 (a whole
-// number of groups of four stages) and at least two tiles per workgroup: one
-// workgroup per CU takes tiles pid, pid + G, pid + 2G, ... (G workgroups, a
-// multiple of the 8 XCDs, so that every tile keeps the XCD the one-tile
-// kernel would give it).  The load pipeline runs on across tiles: the last
-// three stages of a tile, whose loads would lie past its end of K, load the
-// next tile's first three stages (moving to the next tile changes only the
-// loaders' buffer resources, scalar registers).  The next tile therefore
-// starts with its operands in LDS, and no workgroup launch separates the
-// tiles.  The tile's last stage reads nothing of the next one, so that the
-// next tile's fragment registers are free during the epilogue; the epilogue
-// stages 16-bit outputs in the buffer of the tile's last stage (32 rows per
-// wave and pass), the one buffer no load targets at that point.
+// Persistent form of the 256x256 kernel, for whole tiles, K a multiple of 512
+// (a whole number of groups of four stages) and at least one tile per
+// workgroup (the dispatch uses it from three tiles per CU on).  One workgroup
+// per CU takes tiles pid, pid + G, pid + 2G, ... (G workgroups, a multiple of
+// the 8 XCDs, so that every tile keeps the XCD the one-tile kernel would give
+// it).  The load pipeline runs on across tiles: the last three stages of a
+// tile, whose loads would lie past its end of K, load the next tile's first
+// three stages (moving to the next tile changes only the loaders' scalar
+// offset).  The next tile therefore starts with its operands in LDS, and no
+// workgroup launch separates the tiles.  The tile's last stage reads the next
+// tile's first stage and decodes its first step, as any stage does for the
+// one after it, so those fragments stay in registers through the epilogue.
+// The epilogue stages 16-bit outputs in the buffer of the tile's last stage
+// (32 rows per wave and pass), the one buffer no load targets at that point.
 template <int OUT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fast_persistent_kernel(
     int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
@@ -633,7 +635,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fast_persistent_kernel(
   t.init_reads();
 
   // this tile's and the next one's origins (the next one's is computed a
-  // tile ahead, where the fragment registers are free for the arithmetic)
+  // tile ahead, at the tile boundary, not inside the K loop where registers
+  // are scarce)
   const int total = tiles_m * tiles_n;
   int pid = (int)blockIdx.x;
   int64_t m0, n0, nm0 = 0, nn0 = 0;
